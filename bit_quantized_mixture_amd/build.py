@@ -1,0 +1,54 @@
+"""Build the e4b HIP library (libe4b.so) in-tree for gfx950 with hipcc."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libe4b.so")
+SOURCES = ["abi.hip", "pack.hip", "route.hip", "moe.hip"]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the e4b library)")
+
+
+def compile_cmd(out: str) -> list[str]:
+    return [
+        hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+        # correctly rounded float32 division (the NF4 packer divides by absmax) and no
+        # value-changing fast-math
+        "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
+        # keep the compiler from forming packed-fp32 VALU instructions
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wno-unused-command-line-argument",
+        *[os.path.join(CSRC, s) for s in SOURCES],
+        "-o", out,
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB + ".tmp"
+    cmd = compile_cmd(tmp)
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass does not know the packed-fp32 target feature; that warning is harmless
+    noise = "is not a recognized feature for this target"
+    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln and ln.strip()]
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs), file=sys.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

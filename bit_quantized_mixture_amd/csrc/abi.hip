@@ -1,0 +1,213 @@
+// C ABI of the e4b library: host-side validation, workspace carving and kernel launches.
+// Every check runs before anything is enqueued; a failed check enqueues nothing.  There is
+// no alternative code path: on a device other than gfx950 every compute entry point fails.
+#include <string.h>
+
+#include "../../include/e4b.h"
+#include "e4b_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxDevices = 64;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// 1 = gfx950, -1 = other arch, 0 = not yet probed.
+int g_arch_ok[kMaxDevices];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return E4B_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return E4B_ERR_UNSUPPORTED;
+  if (g_arch_ok[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return E4B_ERR_HIP;
+    g_arch_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+  }
+  return g_arch_ok[dev] == 1 ? E4B_OK : E4B_ERR_UNSUPPORTED;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? E4B_OK : E4B_ERR_HIP; }
+
+int check_pack(const void* w, int64_t E, int64_t N, int64_t K, const void* o1, const void* o2,
+               int64_t block) {
+  if (!w || !o1 || !o2) return E4B_ERR_ARG;
+  if (E <= 0 || N <= 0 || K <= 0) return E4B_ERR_ARG;
+  if (K % block) return E4B_ERR_SHAPE;
+  if (!aligned16(w) || !aligned16(o1) || !aligned16(o2)) return E4B_ERR_ALIGN;
+  if (E > (int64_t(1) << 40) / N / K) return E4B_ERR_OVERFLOW;
+  return E4B_OK;
+}
+
+// Row-tile height for the sizes of a forward call (host-known only).
+int pick_bm(const e4b_moe_args* a) {
+  const int64_t S = a->T * a->k;
+  const int path = a->flags & E4B_PATH_MASK;
+  const double mean_rows = double(S) / double(a->E);
+  if (path == E4B_PATH_GEMV || (path == E4B_PATH_AUTO && mean_rows < 16.0)) return 32;
+  return mean_rows >= 384.0 ? 256 : 128;
+}
+
+struct FwdLayout {
+  int bm;
+  int64_t max_mtiles;
+  size_t off_x16, off_h, off_y, off_tiles, off_n, total;
+};
+
+int layout_forward(const e4b_moe_args* a, FwdLayout* L) {
+  const int64_t S = a->T * a->k;
+  L->bm = pick_bm(a);
+  const int64_t n_active_max = a->E < S ? a->E : S;
+  L->max_mtiles = (S + n_active_max * (L->bm - 1)) / L->bm;
+  size_t off = 0;
+  L->off_x16 = off;
+  off += align_up(size_t(a->T) * size_t(a->H) * 2);
+  L->off_h = off;
+  off += align_up(size_t(S) * size_t(a->I) * 2);
+  L->off_y = off;
+  off += align_up(size_t(S) * size_t(a->H) * 4);
+  L->off_tiles = off;
+  off += align_up(size_t(L->max_mtiles) * 16);
+  L->off_n = off;
+  off += kAlign;
+  L->total = off;
+  return E4B_OK;
+}
+
+int check_forward_shape(const e4b_moe_args* a) {
+  if (!a) return E4B_ERR_ARG;
+  if (a->fmt != E4B_FMT_NF4 && a->fmt != E4B_FMT_MXFP4) return E4B_ERR_ARG;
+  if (a->E <= 0 || a->H <= 0 || a->I <= 0 || a->T < 0 || a->k < 1) return E4B_ERR_ARG;
+  if (a->k > a->E) return E4B_ERR_ARG;
+  if ((a->flags & ~E4B_PATH_MASK) != 0 || (a->flags & E4B_PATH_MASK) == 3) return E4B_ERR_ARG;
+  if (a->H % 64 || a->I % 64) return E4B_ERR_SHAPE;
+  if (a->T * a->k >= (int64_t(1) << 31)) return E4B_ERR_OVERFLOW;
+  if (a->E >= (int64_t(1) << 31) || a->H >= (int64_t(1) << 31) || a->I >= (int64_t(1) << 30))
+    return E4B_ERR_OVERFLOW;
+  return E4B_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int e4b_version(void) { return 100; }
+
+const char* e4b_status_string(int status) {
+  switch (status) {
+    case E4B_OK: return "ok";
+    case E4B_ERR_ARG: return "invalid argument (null pointer, bad size, flag or format)";
+    case E4B_ERR_SHAPE: return "shape breaks a block or tiling constraint";
+    case E4B_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case E4B_ERR_WORKSPACE: return "workspace missing or too small";
+    case E4B_ERR_UNSUPPORTED: return "current device is not gfx950";
+    case E4B_ERR_OVERFLOW: return "size overflows the index types";
+    case E4B_ERR_HIP: return "HIP runtime or launch failure";
+    default: return "unknown status";
+  }
+}
+
+int e4b_pack_nf4(const uint16_t* w, int64_t E, int64_t N, int64_t K, uint8_t* packed,
+                 float* absmax, void* stream) {
+  int st = check_pack(w, E, N, K, packed, absmax, 64);
+  if (st != E4B_OK) return st;
+  if ((st = check_device()) != E4B_OK) return st;
+  return launched(e4b::launch_pack_nf4(w, E * N * K, packed, absmax, (hipStream_t)stream));
+}
+
+int e4b_pack_mxfp4(const uint16_t* w, int64_t E, int64_t N, int64_t K, uint8_t* blocks,
+                   uint8_t* scales, void* stream) {
+  int st = check_pack(w, E, N, K, blocks, scales, 32);
+  if (st != E4B_OK) return st;
+  if ((st = check_device()) != E4B_OK) return st;
+  return launched(e4b::launch_pack_mxfp4(w, E * N * K, blocks, scales, (hipStream_t)stream));
+}
+
+int e4b_route_workspace_bytes(int64_t T, int64_t E, int32_t k, size_t* bytes) {
+  if (!bytes) return E4B_ERR_ARG;
+  if (T < 0 || E <= 0 || k < 1) return E4B_ERR_ARG;
+  *bytes = align_up(size_t(E) * 4);
+  return E4B_OK;
+}
+
+int e4b_route_permute(const float* logits, int64_t T, int64_t E, int32_t k, int32_t flags,
+                      int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                      int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || E <= 0 || k < 1 || k > E) return E4B_ERR_ARG;
+  if (E > 1024 || k > 64) return E4B_ERR_SHAPE;
+  if (flags & ~E4B_ROUTE_RENORMALIZE) return E4B_ERR_ARG;
+  if (!expert_offsets || !ws) return E4B_ERR_ARG;
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !sorted_slots)) return E4B_ERR_ARG;
+  if (T * k >= (int64_t(1) << 31)) return E4B_ERR_OVERFLOW;
+  const void* ptrs[] = {logits, topk_ids, topk_w, expert_offsets, sorted_slots, ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return E4B_ERR_ALIGN;
+  size_t need = 0;
+  e4b_route_workspace_bytes(T, E, k, &need);
+  if (ws_bytes < need) return E4B_ERR_WORKSPACE;
+  int st = check_device();
+  if (st != E4B_OK) return st;
+  return launched(e4b::launch_route(logits, T, E, k, (flags & E4B_ROUTE_RENORMALIZE) != 0,
+                                    topk_ids, topk_w, expert_offsets, sorted_slots,
+                                    reinterpret_cast<int32_t*>(ws), (hipStream_t)stream));
+}
+
+int e4b_moe_workspace_bytes(const e4b_moe_args* a, size_t* bytes) {
+  if (!bytes) return E4B_ERR_ARG;
+  int st = check_forward_shape(a);
+  if (st != E4B_OK) return st;
+  FwdLayout L;
+  layout_forward(a, &L);
+  *bytes = L.total;
+  return E4B_OK;
+}
+
+int e4b_moe_forward(const e4b_moe_args* a, void* stream) {
+  int st = check_forward_shape(a);
+  if (st != E4B_OK) return st;
+  if (a->T == 0) return check_device();  // nothing to compute; no buffer is touched
+  if (!a->x || !a->w_gu || !a->s_gu || !a->w_dn || !a->s_dn || !a->topk_w ||
+      !a->expert_offsets || !a->sorted_slots || !a->out || !a->ws)
+    return E4B_ERR_ARG;
+  const void* ptrs[] = {a->x, a->w_gu, a->s_gu, a->w_dn, a->s_dn, a->topk_w,
+                        a->expert_offsets, a->sorted_slots, a->out, a->out_f32, a->ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return E4B_ERR_ALIGN;
+  FwdLayout L;
+  layout_forward(a, &L);
+  if (a->ws_bytes < L.total) return E4B_ERR_WORKSPACE;
+  if ((st = check_device()) != E4B_OK) return st;
+
+  char* ws = reinterpret_cast<char*>(a->ws);
+  e4b::MoeLaunch M{};
+  M.fmt = a->fmt;
+  M.E = a->E;
+  M.H = a->H;
+  M.I = a->I;
+  M.T = a->T;
+  M.k = a->k;
+  M.cfg.bm = L.bm;
+  M.cfg.waves = L.bm == 32 ? 1 : 4;
+  M.max_mtiles = L.max_mtiles;
+  M.x = a->x;
+  M.w_gu = a->w_gu;
+  M.s_gu = a->s_gu;
+  M.w_dn = a->w_dn;
+  M.s_dn = a->s_dn;
+  M.topk_w = a->topk_w;
+  M.offsets = a->expert_offsets;
+  M.slots = a->sorted_slots;
+  M.out = a->out;
+  M.out_f32 = a->out_f32;
+  M.x16 = reinterpret_cast<_Float16*>(ws + L.off_x16);
+  M.h = reinterpret_cast<_Float16*>(ws + L.off_h);
+  M.y = reinterpret_cast<float*>(ws + L.off_y);
+  M.tiles = reinterpret_cast<int32_t*>(ws + L.off_tiles);
+  M.n_mtiles = reinterpret_cast<int32_t*>(ws + L.off_n);
+  return launched(e4b::launch_moe_forward(M, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,113 @@
+// Device-side helpers shared by the e4b kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace e4b {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------------------
+// NF4 codebook (QLoRA NormalFloat-4, ascending, code 0..15) in the two forms used here.
+//
+// (1) Decode table: fp16 rounding of each value, fp16 bits for codes 0..15:
+//     bc00 b992 b833 b652 b48d b1ea add4 0000 2d18 3126 33e0 3568 370d 3880 39c9 3c00
+//     held as a low-byte plane and a high-byte plane, 4 codes per dword (byte i of
+//     kNf4LoQ = low byte of code 4Q+i), so one v_perm_b32 looks up 4 codes of one half
+//     of the table at once.
+constexpr uint32_t kNf4Lo0 = 0x52339200u;
+constexpr uint32_t kNf4Lo1 = 0x00D4EA8Du;
+constexpr uint32_t kNf4Lo2 = 0x68E02618u;
+constexpr uint32_t kNf4Lo3 = 0x00C9800Du;
+constexpr uint32_t kNf4Hi0 = 0xB6B8B9BCu;
+constexpr uint32_t kNf4Hi1 = 0x00ADB1B4u;
+constexpr uint32_t kNf4Hi2 = 0x3533312Du;
+constexpr uint32_t kNf4Hi3 = 0x3C393837u;
+
+// (2) Quantise thresholds: for the float32 codebook values C[j] (bit patterns
+//     bf800000 bf3239b1 bf066b30 beca32a0 be91a24d be3d353f bdba7871 00000000
+//     3da2faff 3e24cae3 3e7c04dd 3ead033a 3ee1a4b8 3f1007ab 3f3913b3 3f800000),
+//     kNf4Up[j] is the smallest float32 strictly above the exact midpoint
+//     (C[j] + C[j+1]) / 2.  For a float32 n, "n is nearer C[j+1], or tied and not
+//     lower" reduces to n >= kNf4Up[j], so code = #{j : n >= kNf4Up[j]} is the nearest
+//     code with exact ties going to the lower code.
+__device__ __constant__ const uint32_t kNf4Up[15] = {
+    0xBF591CD8u, 0xBF1C5270u, 0xBEEB847Fu, 0xBEADEA76u, 0xBE703CECu,
+    0xBE0D38BBu, 0xBD3A7870u, 0x3D22FB00u, 0x3DF64863u, 0x3E5067E1u,
+    0x3E9582D5u, 0x3EC753FAu, 0x3F006D04u, 0x3F248DB0u, 0x3F5C89DAu};
+
+// Order in which nf4_decode8 leaves the 8 elements of a packed dword in its 4 output
+// registers (two fp16 per register): slot i holds element kNf4SlotElem[i].  Activation
+// operands are stored with the same order inside every aligned group of 8 elements so
+// the MFMA k-slots of both operands line up.
+//   slot:    0 1 2 3 4 5 6 7
+//   element: 0 2 4 6 1 3 5 7
+// Inverse (element e lives in slot kNf4ElemSlot[e]): 0 4 1 5 2 6 3 7.
+__host__ __device__ constexpr int nf4_elem_slot(int e) { return (e >> 1) | ((e & 1) << 2); }
+
+__device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) {
+  return __builtin_amdgcn_perm(s0, s1, sel);
+}
+
+// Bitfield select: bits of a where mask is 1, bits of b elsewhere (v_bfi_b32).
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) {
+  return (mask & a) | (~mask & b);
+}
+
+// Decode one packed NF4 dword (8 codes, element 2b in the high nibble of byte b, 2b+1 in
+// the low nibble) to 8 fp16 codebook values, in slot order (see kNf4SlotElem).
+__device__ __forceinline__ void nf4_decode8(uint32_t w, uint32_t out[4]) {
+  const uint32_t s_odd = w & 0x07070707u;              // low nibbles: elements 1,3,5,7
+  const uint32_t s_even = (w >> 4) & 0x07070707u;      // high nibbles: elements 0,2,4,6
+  // 0xFF in every byte whose code is >= 8: selector 0x0c gives 0x00, 0x0d gives 0xFF.
+  const uint32_t m_odd = perm(0u, 0u, ((w >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
+  const uint32_t m_even = perm(0u, 0u, ((w >> 7) & 0x01010101u) | 0x0C0C0C0Cu);
+  const uint32_t lo_odd = bfi(m_odd, perm(kNf4Lo3, kNf4Lo2, s_odd), perm(kNf4Lo1, kNf4Lo0, s_odd));
+  const uint32_t hi_odd = bfi(m_odd, perm(kNf4Hi3, kNf4Hi2, s_odd), perm(kNf4Hi1, kNf4Hi0, s_odd));
+  const uint32_t lo_even = bfi(m_even, perm(kNf4Lo3, kNf4Lo2, s_even), perm(kNf4Lo1, kNf4Lo0, s_even));
+  const uint32_t hi_even = bfi(m_even, perm(kNf4Hi3, kNf4Hi2, s_even), perm(kNf4Hi1, kNf4Hi0, s_even));
+  // interleave low/high byte planes into fp16 pairs
+  out[0] = perm(hi_even, lo_even, 0x05010400u);  // elements 0, 2
+  out[1] = perm(hi_even, lo_even, 0x07030602u);  // elements 4, 6
+  out[2] = perm(hi_odd, lo_odd, 0x05010400u);    // elements 1, 3
+  out[3] = perm(hi_odd, lo_odd, 0x07030602u);    // elements 5, 7
+}
+
+// Multiply two packed fp16 by the same fp16 scale (v_pk_mul_f16).
+__device__ __forceinline__ uint32_t pk_mul_f16(uint32_t v, f16x2 s) {
+  f16x2 r = __builtin_bit_cast(f16x2, v) * s;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Decode one MXFP4 dword (8 e2m1 codes, element 2b in the low nibble of byte b) to 8
+// fp16 values times `scale` (a power of two), natural element order.
+__device__ __forceinline__ void mxfp4_decode8(uint32_t w, float scale, uint32_t out[4]) {
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 0));
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 1));
+  out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 2));
+  out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, scale, 3));
+}
+
+// e8m0 byte -> float32 power of two 2^(b-127) (b = 0 gives 2^-127, a float32 subnormal).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+  return b == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(b << 23);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// float32 -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+}  // namespace e4b

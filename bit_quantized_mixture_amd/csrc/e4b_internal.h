@@ -1,0 +1,53 @@
+// Host-side launchers shared between the kernel translation units and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace e4b {
+
+// Tile shapes of the grouped expert GEMM.  BM = rows (routed slots) per tile; the N extent
+// per workgroup is 32 h-columns per wave for gate_up (a 32-wide gate fragment and the
+// matching 32-wide up fragment) and 64 output columns per wave for down.
+struct TileCfg {
+  int bm;
+  int waves;
+};
+
+hipError_t launch_pack_nf4(const uint16_t* w, int64_t n_elems, uint8_t* packed, float* absmax,
+                           hipStream_t stream);
+hipError_t launch_pack_mxfp4(const uint16_t* w, int64_t n_elems, uint8_t* blocks, uint8_t* scales,
+                             hipStream_t stream);
+
+// Routing: counts (E int32) live in the workspace.
+hipError_t launch_route(const float* logits, int64_t T, int64_t E, int k, bool renorm,
+                        int32_t* ids, float* w, int32_t* offsets, int32_t* slots, int32_t* counts,
+                        hipStream_t stream);
+
+struct MoeLaunch {
+  int fmt;
+  int64_t E, H, I, T;
+  int k;
+  TileCfg cfg;
+  int64_t max_mtiles;
+  const uint16_t* x;
+  const uint8_t* w_gu;
+  const void* s_gu;
+  const uint8_t* w_dn;
+  const void* s_dn;
+  const float* topk_w;
+  const int32_t* offsets;
+  const int32_t* slots;
+  uint16_t* out;
+  float* out_f32;
+  // workspace carve-outs
+  _Float16* x16;   // [T, H]
+  _Float16* h;     // [S, I]
+  float* y;        // [S, H]
+  int32_t* tiles;  // [max_mtiles, 4]
+  int32_t* n_mtiles;
+};
+
+hipError_t launch_moe_forward(const MoeLaunch& L, hipStream_t stream);
+
+}  // namespace e4b

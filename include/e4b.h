@@ -1,0 +1,166 @@
+/*
+ * e4b.h — C ABI of a fused Mixture-of-Experts layer on 4-bit expert weights, for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes, on one GPU, the expert part of a MoE layer whose fused expert
+ * stacks gate_up_proj [E, 2I, H] and down_proj [E, H, I] (rows = output features,
+ * columns = input features, the transformers-v5 layout described in the experts4bit-qlora
+ * 0.35.0 project description) are stored as 4-bit codes:
+ *
+ *   NF4   — 16-entry NormalFloat codebook, one float32 absmax per 64 consecutive weights
+ *           of a row, two codes per byte (bitsandbytes pull request #1984, Summary and
+ *           Design; grouped-nf4-gemm 0.25.0 project description, opening section and
+ *           "Try it on CPU right now" example 1).
+ *   MXFP4 — OCP e2m1 codes with one e8m0 scale byte per 32 consecutive weights of a row
+ *           (grouped-nf4-gemm 0.25.0 project description, opening section and "Try it on
+ *           CPU right now" example 2).
+ *
+ * The forward multiplies directly on the packed bytes: codes are decoded in registers
+ * and scaled per block, products accumulate in fp32, and only the final output is
+ * rounded to bf16 (grouped-nf4-gemm 0.25.0 project description, opening section).  No
+ * dequantised copy of a weight is ever written.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers, owned by the caller, row-major and dense.
+ *     The library allocates and frees nothing and keeps no state between calls; calls
+ *     on different streams may run concurrently if their buffers do not overlap.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work
+ *     and return; results are visible after the caller synchronises the stream.
+ *   - Arguments are validated on the host before anything is enqueued.  A failed check
+ *     returns a negative e4b_status and enqueues nothing.  There is no fallback path:
+ *     either the gfx950 kernels run or the call fails.
+ *   - Every pointer must be 16-byte aligned.  bf16 values are passed as uint16_t bits.
+ *   - Faults inside kernels surface at the caller's next synchronisation; launch
+ *     failures return E4B_ERR_HIP.
+ */
+#ifndef E4B_H_
+#define E4B_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum e4b_status {
+  E4B_OK = 0,
+  E4B_ERR_ARG = -1,         /* NULL pointer, non-positive size, bad flag or format */
+  E4B_ERR_SHAPE = -2,       /* a dimension breaks a block or tiling constraint */
+  E4B_ERR_ALIGN = -3,       /* a pointer is not 16-byte aligned */
+  E4B_ERR_WORKSPACE = -4,   /* workspace missing or smaller than the queried size */
+  E4B_ERR_UNSUPPORTED = -5, /* current device is not gfx950 */
+  E4B_ERR_OVERFLOW = -6,    /* a count does not fit the index types (T*k >= 2^31, ...) */
+  E4B_ERR_HIP = -7          /* a HIP runtime call or kernel launch failed */
+} e4b_status;
+
+typedef enum e4b_fmt { E4B_FMT_NF4 = 0, E4B_FMT_MXFP4 = 1 } e4b_fmt;
+
+/* e4b_route_permute flags */
+#define E4B_ROUTE_RENORMALIZE 0x1 /* softmax over the chosen k logits (default reading) */
+
+/* e4b_moe_args.flags: execution path (bits 0-1).  AUTO picks the small-M streaming path
+ * when the mean routed rows per expert T*k/E is below 16, the MFMA tile path otherwise.
+ * The choice depends only on host-known sizes; no device value is read back. */
+#define E4B_PATH_AUTO 0x0
+#define E4B_PATH_GEMM 0x1 /* MFMA grouped GEMM, 256-row tiles */
+#define E4B_PATH_GEMV 0x2 /* small-M streaming path, 32-row tiles */
+#define E4B_PATH_MASK 0x3
+
+/*
+ * e4b_pack_nf4 — quantise bf16 expert stacks to NF4.
+ *   w       [E, N, K] bf16 (uint16 bits).  K % 64 == 0.
+ *   packed  [E, N, K/2] uint8 out.  Byte p of a row holds codes of elements 2p (high
+ *           nibble) and 2p+1 (low nibble).
+ *   absmax  [E, N, K/64] float32 out: max |w| over each 64-block.
+ * Per block: n = w / absmax (float32, correctly rounded); code = index of the nearest
+ * codebook value, an exact tie taking the lower code; an all-zero block gets absmax 0
+ * and code 7 (zero).  Defined by the pages cited above (per-expert blockwise absmax,
+ * [N, K] -> [N, K/2] uint8 + [N, K/64] float32).  Bit-exact and deterministic.
+ */
+int e4b_pack_nf4(const uint16_t* w, int64_t E, int64_t N, int64_t K,
+                 uint8_t* packed, float* absmax, void* stream);
+
+/*
+ * e4b_pack_mxfp4 — quantise bf16 expert stacks to MXFP4 (OCP MX v1.0 conversion).
+ *   w       [E, N, K] bf16 bits.  K % 32 == 0.
+ *   blocks  [E, N, K/32, 16] uint8 out.  Byte p of a block holds element 2p in the low
+ *           nibble and 2p+1 in the high nibble (released-checkpoint order).
+ *   scales  [E, N, K/32] uint8 out: e8m0 byte = shared exponent + 127, where the shared
+ *           exponent is floor(log2(amax)) - 2 clamped to [-127, 127] (-127 for an
+ *           all-zero block).  Elements are w / 2^exponent rounded to the nearest e2m1
+ *           value (ties to even, saturating at 6), sign kept.  Bit-exact.
+ */
+int e4b_pack_mxfp4(const uint16_t* w, int64_t E, int64_t N, int64_t K,
+                   uint8_t* blocks, uint8_t* scales, void* stream);
+
+/* Workspace bytes e4b_route_permute needs for (T, E, k). */
+int e4b_route_workspace_bytes(int64_t T, int64_t E, int32_t k, size_t* bytes);
+
+/*
+ * e4b_route_permute — top-k routing and the expert-major slot order (the router
+ * epilogue among the grouped-nf4-gemm 0.25.0 glue kernels, project description opening
+ * section).
+ *   logits          [T, E] float32, finite.
+ *   k               1 <= k <= E, k <= 64.  E <= 1024.  T*k < 2^31.
+ *   topk_ids        [T, k] int32 out: per token the k largest logits in descending
+ *                   order, equal logits ordered by the lower expert index.
+ *   topk_w          [T, k] float32 out: softmax over the chosen k logits (flag
+ *                   E4B_ROUTE_RENORMALIZE), or the full softmax probabilities of the
+ *                   chosen experts (flag clear).
+ *   expert_offsets  [E+1] int32 out: exclusive prefix sum of per-expert slot counts.
+ *   sorted_slots    [T*k] int32 out: slot ids s = t*k + j ordered by expert, then token.
+ *   ws, ws_bytes    device workspace of at least e4b_route_workspace_bytes().
+ * ids, offsets and slots are bit-exact and deterministic.
+ */
+int e4b_route_permute(const float* logits, int64_t T, int64_t E, int32_t k, int32_t flags,
+                      int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                      int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream);
+
+/* Arguments of e4b_moe_forward.  Sizes: H % 64 == 0, I % 64 == 0 (both formats). */
+typedef struct e4b_moe_args {
+  int32_t fmt;            /* e4b_fmt */
+  int32_t k;              /* experts per token, as given to e4b_route_permute */
+  int64_t E, H, I, T;
+  const uint16_t* x;      /* [T, H] bf16 bits; values must lie in fp16 range */
+  const uint8_t* w_gu;    /* NF4 [E, 2I, H/2]  | MXFP4 [E, 2I, H/32, 16]; rows 0..I-1 gate, I..2I-1 up */
+  const void* s_gu;       /* NF4 float [E, 2I, H/64] | MXFP4 uint8 [E, 2I, H/32] */
+  const uint8_t* w_dn;    /* NF4 [E, H, I/2]   | MXFP4 [E, H, I/32, 16] */
+  const void* s_dn;       /* NF4 float [E, H, I/64]  | MXFP4 uint8 [E, H, I/32] */
+  const float* topk_w;    /* [T, k] routing weights from e4b_route_permute */
+  const int32_t* expert_offsets; /* [E+1] from e4b_route_permute */
+  const int32_t* sorted_slots;   /* [T*k] from e4b_route_permute */
+  uint16_t* out;          /* [T, H] bf16 out: RNE of the fp32 result */
+  float* out_f32;         /* [T, H] float32 out, or NULL: the value `out` is rounded from */
+  void* ws;               /* device workspace of at least e4b_moe_workspace_bytes() */
+  size_t ws_bytes;
+  int32_t flags;          /* E4B_PATH_* */
+  int32_t reserved;
+} e4b_moe_args;
+
+/* Workspace bytes e4b_moe_forward needs for the sizes, format and flags in `a`. */
+int e4b_moe_workspace_bytes(const e4b_moe_args* a, size_t* bytes);
+
+/*
+ * e4b_moe_forward — the MoE expert layer on packed weights.
+ * For every token t: out[t] = sum_j topk_w[t,j] * down_e( silu(gate_e(x_t)) * up_e(x_t) )
+ * with e = the expert of slot t*k+j (bitsandbytes pull request #1984, Design: per-expert
+ * SwiGLU MLP; grouped-nf4-gemm 0.25.0, opening section: one launch over all active
+ * experts, table decode, block scaling, fp32 accumulation, bf16 epilogue).
+ * Matrix products use fp16 operands (x converted exactly from bf16; decoded weights and
+ * the SwiGLU activation rounded to fp16) with fp32 accumulation; the combine is fp32 in
+ * a fixed order, so results are deterministic run to run.
+ */
+int e4b_moe_forward(const e4b_moe_args* a, void* stream);
+
+/* Static description of a status code. */
+const char* e4b_status_string(int status);
+
+/* Library version, as MAJOR*10000 + MINOR*100 + PATCH. */
+int e4b_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* E4B_H_ */

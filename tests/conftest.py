@@ -11,3 +11,14 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: large CPU work (full-size sampled checks)")
+
+
+@pytest.fixture(scope="session")
+def e4b():
+    """The binding, with libe4b.so built in-tree first if it is missing."""
+    lib = os.path.join(ROOT, "bit_quantized_mixture_amd", "libe4b.so")
+    if not os.path.exists(lib):
+        from bit_quantized_mixture_amd.build import build
+        build()
+    import bit_quantized_mixture_amd as m
+    return m

@@ -1,0 +1,123 @@
+"""Host-only checks of the C ABI: the library loads, exports every entry point that
+include/e4b.h declares, and rejects bad arguments before touching a device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "e4b.h")
+ERR_ARG, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_OVERFLOW = -1, -2, -3, -4, -5, -6
+FAKE = 0x100000  # aligned, never dereferenced: every call below fails validation first
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(e4b_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("e4b_pack_nf4", "e4b_pack_mxfp4", "e4b_route_permute", "e4b_moe_forward",
+              "e4b_route_workspace_bytes", "e4b_moe_workspace_bytes", "e4b_status_string", "e4b_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(e4b):
+    lib = ctypes.CDLL(e4b.lib_path)
+    for n in _declared():
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", e4b.lib_path], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (e4b_\w+)", out))
+    assert set(_declared()) <= exported
+
+
+def test_version_and_status_strings(e4b):
+    assert e4b.e4b_version() >= 100
+    for s in range(-7, 1):
+        assert e4b.e4b_status_string(s) and e4b.e4b_status_string(s) != "unknown status"
+
+
+def _pack(e4b, fn, w=FAKE, E=2, N=4, K=128, o1=FAKE, o2=FAKE):
+    c = e4b._c_pack_nf4 if fn == "nf4" else e4b._c_pack_mxfp4
+    return c(w, E, N, K, o1, o2, None)
+
+
+@pytest.mark.parametrize("fn,block", [("nf4", 64), ("mxfp4", 32)])
+def test_pack_rejects_bad_arguments(e4b, fn, block):
+    assert _pack(e4b, fn, w=None) == ERR_ARG
+    assert _pack(e4b, fn, o1=None) == ERR_ARG
+    assert _pack(e4b, fn, o2=None) == ERR_ARG
+    assert _pack(e4b, fn, E=0) == ERR_ARG
+    assert _pack(e4b, fn, N=-1) == ERR_ARG
+    assert _pack(e4b, fn, K=block + block // 2) == ERR_SHAPE
+    assert _pack(e4b, fn, w=FAKE + 8) == ERR_ALIGN
+    assert _pack(e4b, fn, o1=FAKE + 4) == ERR_ALIGN
+    assert _pack(e4b, fn, E=1 << 30, N=1 << 12, K=1 << 12) == ERR_OVERFLOW
+
+
+def test_route_rejects_bad_arguments(e4b):
+    def call(T=16, E=8, k=2, flags=1, ws_bytes=4096, **p):
+        ptr = dict(logits=FAKE, ids=FAKE, w=FAKE, off=FAKE, slots=FAKE, ws=FAKE)
+        ptr.update(p)
+        return e4b._c_route(ptr["logits"], T, E, k, flags, ptr["ids"], ptr["w"], ptr["off"],
+                            ptr["slots"], ptr["ws"], ws_bytes, None)
+    assert call(k=0) == ERR_ARG
+    assert call(k=9) == ERR_ARG
+    assert call(E=0) == ERR_ARG
+    assert call(T=-1) == ERR_ARG
+    assert call(flags=2) == ERR_ARG
+    assert call(E=2048, k=2) == ERR_SHAPE
+    assert call(E=128, k=65) == ERR_SHAPE
+    assert call(logits=None) == ERR_ARG
+    assert call(off=None) == ERR_ARG
+    assert call(ws=None) == ERR_ARG
+    assert call(slots=FAKE + 2) == ERR_ALIGN
+    assert call(ws_bytes=0) == ERR_WORKSPACE
+    assert call(T=1 << 29, k=8) == ERR_OVERFLOW
+    assert e4b.e4b_route_workspace_bytes(16, 8, 2) >= 32
+
+
+def _args(e4b, **kw):
+    a = e4b.MoeArgs()
+    a.fmt, a.k, a.E, a.H, a.I, a.T = 0, 2, 8, 256, 512, 64
+    for f in ("x", "w_gu", "s_gu", "w_dn", "s_dn", "topk_w", "expert_offsets", "sorted_slots", "out", "ws"):
+        setattr(a, f, FAKE)
+    a.out_f32 = None
+    a.ws_bytes = 1 << 40
+    a.flags = 0
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_forward_rejects_bad_arguments(e4b):
+    f = lambda **kw: e4b._c_moe_forward(ctypes.byref(_args(e4b, **kw)), None)
+    assert f(fmt=2) == ERR_ARG
+    assert f(k=0) == ERR_ARG
+    assert f(k=9) == ERR_ARG
+    assert f(E=0) == ERR_ARG
+    assert f(T=-1) == ERR_ARG
+    assert f(flags=3) == ERR_ARG
+    assert f(flags=4) == ERR_ARG
+    assert f(H=96) == ERR_SHAPE
+    assert f(I=100) == ERR_SHAPE
+    assert f(x=None) == ERR_ARG
+    assert f(s_dn=None) == ERR_ARG
+    assert f(ws=None) == ERR_ARG
+    assert f(out=FAKE + 2) == ERR_ALIGN
+    assert f(out_f32=FAKE + 4) == ERR_ALIGN
+    assert f(ws_bytes=1024) == ERR_WORKSPACE
+    assert f(T=1 << 28, k=8) == ERR_OVERFLOW
+
+
+def test_workspace_sizes_cover_the_intermediates(e4b):
+    from moe_inputs import WORKLOADS
+    for wl in WORKLOADS.values():
+        n = e4b.e4b_moe_workspace_bytes(wl.fmt, wl.E, wl.H, wl.I, wl.T, wl.k)
+        S = wl.T * wl.k
+        assert n >= 2 * wl.T * wl.H + 2 * S * wl.I + 4 * S * wl.H
+        assert n < 2 * (2 * wl.T * wl.H + 2 * S * wl.I + 4 * S * wl.H) + (1 << 20)

@@ -1,0 +1,85 @@
+"""GPU MoE forward vs the float64 oracle, to the per-row tolerance
+max|gpu - oracle| <= 8e-3 * ||oracle row||_2 / sqrt(H) + 1e-3, applied to the float32 value
+the bf16 output is rounded from; the bf16 output must be that value rounded to nearest even."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import (Layer, assert_out_is_rne_of_f32, assert_rows_within_tolerance,
+                         random_layer)
+from moe_inputs import WORKLOADS, make_logits, make_weights, make_x
+
+pytestmark = pytest.mark.gpu
+
+PATHS = {"auto": 0, "gemm": 1, "gemv": 2}
+
+
+@pytest.fixture(scope="module")
+def tiny(e4b):
+    wl = WORKLOADS["tiny_nf4"]
+    return Layer(e4b, "nf4", make_x(wl), make_logits(wl), make_weights(wl, "gate_up"),
+                 make_weights(wl, "down"), wl.k)
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_tiny_nf4_all_tokens(tiny, path):
+    out, out32 = tiny.forward(PATHS[path])
+    ref = tiny.oracle_out()
+    assert_rows_within_tolerance(out32, ref, f"tiny_nf4/{path}")
+    assert_out_is_rne_of_f32(out, out32)
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("E,H,I,T,k", [
+    (8, 256, 512, 64, 2),      # the tiny workload's shape
+    (3, 320, 192, 37, 2),      # ragged: I not a multiple of the N tile, T odd
+    (5, 128, 64, 300, 5),      # k = E, several M tiles per expert
+    (16, 64, 128, 9, 4),       # most experts empty
+    (1, 192, 128, 40, 1),      # one expert: a dense SwiGLU MLP
+    (2, 128, 128, 700, 2),     # >= 384 rows per expert: 256-row tiles, ragged last tile
+])
+def test_small_layers(e4b, fmt, path, E, H, I, T, k):
+    layer = random_layer(e4b, fmt, E, H, I, T, k, seed=E * 7 + T)
+    out, out32 = layer.forward(PATHS[path])
+    assert_rows_within_tolerance(out32, layer.oracle_out(), f"{fmt}/{path}/{E},{H},{I},{T},{k}")
+    assert_out_is_rne_of_f32(out, out32)
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
+def test_skewed_routing_with_empty_experts_and_a_hot_expert(e4b, fmt):
+    E = 12
+    bias = np.full(E, -30.0)
+    bias[3] = 10.0                                    # every token picks expert 3 ...
+    bias[7] = 5.0                                     # ... and 7; the rest are empty
+    layer = random_layer(e4b, fmt, E, 256, 256, 600, 2, seed=5, logit_bias=bias)
+    for path in PATHS.values():
+        out, out32 = layer.forward(path)
+        assert_rows_within_tolerance(out32, layer.oracle_out(), f"{fmt}/skewed/{path}")
+
+
+def test_paths_agree_and_are_deterministic(tiny):
+    a = tiny.forward(1)
+    b = tiny.forward(1)
+    assert np.array_equal(a[1], b[1]) and np.array_equal(a[0], b[0])
+    c = tiny.forward(2)
+    d = tiny.forward(2)
+    assert np.array_equal(c[1], d[1])
+
+
+def test_empty_batch(e4b, tiny):
+    x = torch.zeros((0, tiny.H), dtype=torch.bfloat16, device="cuda:0")
+    lg = torch.zeros((0, tiny.E), dtype=torch.float32, device="cuda:0")
+    ids, w, off, slots = e4b.e4b_route_permute(lg, tiny.k)
+    out, _ = e4b.e4b_moe_forward("nf4", x, tiny.gp, tiny.gs, tiny.dp, tiny.ds, w, off, slots, tiny.k)
+    torch.cuda.synchronize()
+    assert out.shape == (0, tiny.H)
+
+
+def test_zero_input_gives_zero_output(e4b, tiny):
+    x = torch.zeros_like(tiny.x)
+    ids, w, off, slots = tiny.route()
+    out, out32 = e4b.e4b_moe_forward("nf4", x, tiny.gp, tiny.gs, tiny.dp, tiny.ds, w, off, slots,
+                                     tiny.k, out_f32=True)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out32).item() == 0
