@@ -42,7 +42,7 @@ class MoeArgs(ctypes.Structure):
         ("x", _vp), ("w_gu", _vp), ("s_gu", _vp), ("w_dn", _vp), ("s_dn", _vp),
         ("topk_w", _vp), ("expert_offsets", _vp), ("sorted_slots", _vp),
         ("out", _vp), ("out_f32", _vp), ("ws", _vp), ("ws_bytes", _sz),
-        ("flags", _i32), ("reserved", _i32),
+        ("flags", _i32), ("reserved", _i32), ("stage_events", ctypes.POINTER(_vp)),
     ]
 
 
@@ -184,10 +184,13 @@ def e4b_moe_workspace_bytes(fmt, E: int, H: int, I: int, T: int, k: int, path: i
 
 
 def e4b_moe_forward(fmt, x, w_gu, s_gu, w_dn, s_dn, topk_w, expert_offsets, sorted_slots, k: int,
-                    out=None, out_f32=None, ws=None, path: int = E4B_PATH_AUTO, stream=None):
+                    out=None, out_f32=None, ws=None, path: int = E4B_PATH_AUTO, stream=None,
+                    stage_events=None):
     """MoE expert layer on packed weights.  Returns (out bf16 [T, H], out_f32 or None).
 
     `out_f32`: pass True to allocate the float32 output, a tensor to fill it, None to skip.
+    `stage_events`: None, or 6 torch.cuda.Event (enable_timing=True), each recorded once
+    beforehand so that it exists; the call records them around its 5 stages.
     """
     _need(x, "x", _BF16)
     T, H = x.shape
@@ -203,5 +206,10 @@ def e4b_moe_forward(fmt, x, w_gu, s_gu, w_dn, s_dn, topk_w, expert_offsets, sort
         ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
     a = _moe_args(fmt, x, w_gu, s_gu, w_dn, s_dn, topk_w, expert_offsets, sorted_slots, E, H, I, k,
                   out, out_f32, ws, path)
+    if stage_events is not None:
+        if len(stage_events) != 6:
+            raise ValueError("stage_events needs 6 events")
+        handles = (_vp * 6)(*[ev.cuda_event for ev in stage_events])
+        a.stage_events = ctypes.cast(handles, ctypes.POINTER(_vp))
     _check("e4b_moe_forward", _c_moe_forward(ctypes.byref(a), _stream(stream)))
     return out, out_f32

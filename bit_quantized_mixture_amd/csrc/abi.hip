@@ -83,6 +83,7 @@ int check_forward_shape(const e4b_moe_args* a) {
   if (a->E <= 0 || a->H <= 0 || a->I <= 0 || a->T < 0 || a->k < 1) return E4B_ERR_ARG;
   if (a->k > a->E) return E4B_ERR_ARG;
   if ((a->flags & ~E4B_PATH_MASK) != 0 || (a->flags & E4B_PATH_MASK) == 3) return E4B_ERR_ARG;
+  if (a->reserved != 0) return E4B_ERR_ARG;
   if (a->H % 64 || a->I % 64) return E4B_ERR_SHAPE;
   if (a->T * a->k >= (int64_t(1) << 31)) return E4B_ERR_OVERFLOW;
   if (a->E >= (int64_t(1) << 31) || a->H >= (int64_t(1) << 31) || a->I >= (int64_t(1) << 30))
@@ -207,6 +208,7 @@ int e4b_moe_forward(const e4b_moe_args* a, void* stream) {
   M.y = reinterpret_cast<float*>(ws + L.off_y);
   M.tiles = reinterpret_cast<int32_t*>(ws + L.off_tiles);
   M.n_mtiles = reinterpret_cast<int32_t*>(ws + L.off_n);
+  M.events = a->stage_events;
   return launched(e4b::launch_moe_forward(M, (hipStream_t)stream));
 }
 

@@ -46,6 +46,7 @@ struct MoeLaunch {
   float* y;        // [S, H]
   int32_t* tiles;  // [max_mtiles, 4]
   int32_t* n_mtiles;
+  void* const* events;  // nullable: 6 hipEvent_t around the 5 stages
 };
 
 hipError_t launch_moe_forward(const MoeLaunch& L, hipStream_t stream);

@@ -318,6 +318,10 @@ static unsigned grid_1d(int64_t work, int per_block = 256) {
   return unsigned(g);
 }
 
+static void record(const MoeLaunch& L, int i, hipStream_t stream) {
+  if (L.events) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(L.events[i]), stream);
+}
+
 template <int FMT, int BM, int WAVES>
 static hipError_t launch_gemms(const MoeLaunch& L, hipStream_t stream) {
   GemmArgs g{};
@@ -337,6 +341,7 @@ static hipError_t launch_gemms(const MoeLaunch& L, hipStream_t stream) {
   g.n_ntiles = int((L.I + WAVES * 32 - 1) / (WAVES * 32));
   hipLaunchKernelGGL((moe_gemm_kernel<FMT, true, BM, WAVES>),
                      dim3(unsigned(L.max_mtiles * g.n_ntiles)), dim3(WAVES * 64), 0, stream, g);
+  record(L, 3, stream);
   // down + routing weight
   g.a = L.h;
   g.wq = L.w_dn;
@@ -352,10 +357,13 @@ static hipError_t launch_gemms(const MoeLaunch& L, hipStream_t stream) {
 
 template <int FMT>
 static hipError_t launch_fmt(const MoeLaunch& L, hipStream_t stream) {
+  record(L, 0, stream);
   hipLaunchKernelGGL(convert_x_kernel<FMT>, dim3(grid_1d(L.T * L.H / 8)), dim3(256), 0, stream,
                      L.x, L.x16, L.T * L.H / 8);
+  record(L, 1, stream);
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, stream, L.offsets, int(L.E),
                      L.cfg.bm, L.tiles, L.n_mtiles);
+  record(L, 2, stream);
   hipError_t err;
   if (L.cfg.bm == 256)
     err = launch_gemms<FMT, 256, 4>(L, stream);
@@ -364,8 +372,10 @@ static hipError_t launch_fmt(const MoeLaunch& L, hipStream_t stream) {
   else
     err = launch_gemms<FMT, 32, 1>(L, stream);
   if (err != hipSuccess) return err;
+  record(L, 4, stream);
   hipLaunchKernelGGL(combine_kernel, dim3(grid_1d(L.T * L.H / 4)), dim3(256), 0, stream, L.y, L.T,
                      L.H, L.k, L.out, L.out_f32);
+  record(L, 5, stream);
   return hipGetLastError();
 }
 

@@ -135,7 +135,11 @@ typedef struct e4b_moe_args {
   void* ws;               /* device workspace of at least e4b_moe_workspace_bytes() */
   size_t ws_bytes;
   int32_t flags;          /* E4B_PATH_* */
-  int32_t reserved;
+  int32_t reserved;       /* must be 0 */
+  /* NULL, or 6 hipEvent_t the call records on `stream` around its 5 stages (x conversion,
+   * tile map, gate_up GEMM, down GEMM, combine), so a caller can time each kernel on the
+   * stream it runs on.  Events are created and owned by the caller. */
+  void* const* stage_events;
 } e4b_moe_args;
 
 /* Workspace bytes e4b_moe_forward needs for the sizes, format and flags in `a`. */

@@ -59,14 +59,20 @@ def shared_exponent(amax: np.ndarray) -> np.ndarray:
 
 def round_e2m1_magnitude(q: np.ndarray) -> np.ndarray:
     """Nearest e2m1 magnitude code (0..7) of |q|; ties to the even code; saturate at 6."""
-    m = np.abs(np.asarray(q, np.float64))
-    d = np.abs(m[..., None] - E2M1_MAG)                  # exact for these dyadic values
-    best = d.min(axis=-1, keepdims=True)
-    cand = d == best
-    # among equally near codes (at most two), take the even one
-    even = cand & ((np.arange(8) % 2) == 0)
-    pick = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
-    return np.where(m >= 6.0, 7, pick).astype(np.uint8)
+    m_all = np.abs(np.asarray(q, np.float64))
+    flat = m_all.reshape(-1)
+    out = np.empty(flat.shape, np.uint8)
+    step = 1 << 20                       # bounded memory; element-wise, so chunking is exact
+    for i in range(0, flat.size, step):
+        m = flat[i:i + step]
+        d = np.abs(m[:, None] - E2M1_MAG)                # exact for these dyadic values
+        best = d.min(axis=-1, keepdims=True)
+        cand = d == best
+        # among equally near codes (at most two), take the even one
+        even = cand & ((np.arange(8) % 2) == 0)
+        pick = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+        out[i:i + step] = np.where(m >= 6.0, 7, pick)
+    return out.reshape(m_all.shape)
 
 
 def quantize_pack(w, block: int = BLOCK):

@@ -49,9 +49,15 @@ def nearest_code(n: np.ndarray) -> np.ndarray:
     involved at every tie, so an exact midpoint compares equal and argmin's first-minimum
     rule picks the lower code.
     """
-    n64 = np.asarray(n, dtype=np.float32).astype(np.float64)
-    d = np.abs(n64[..., None] - NF4_CODEBOOK.astype(np.float64))
-    return np.argmin(d, axis=-1).astype(np.uint8)
+    n32 = np.asarray(n, dtype=np.float32)
+    flat = n32.reshape(-1)
+    out = np.empty(flat.shape, np.uint8)
+    cb = NF4_CODEBOOK.astype(np.float64)
+    step = 1 << 20                       # bounded memory; element-wise, so chunking is exact
+    for i in range(0, flat.size, step):
+        d = np.abs(flat[i:i + step].astype(np.float64)[:, None] - cb)
+        out[i:i + step] = np.argmin(d, axis=-1)
+    return out.reshape(n32.shape)
 
 
 def quantize_pack(w, block: int = BLOCK):
