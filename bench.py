@@ -76,13 +76,15 @@ class Resident:
         torch.cuda.synchronize()
         log(f"[bench] {wl.name}: resident in {time.time() - t0:.1f}s (pack {self.pack_s * 1e3:.1f} ms)")
 
+    flags = 0
+
     def step(self, events=None):
         wl = self.wl
         ids, w, off, slots = self.e4b.e4b_route_permute(self.logits, wl.k, ws=self.route_ws)
         gp, gs = self.packed["gate_up"]
         dp, ds = self.packed["down"]
         self.e4b.e4b_moe_forward(wl.fmt, self.x, gp, gs, dp, ds, w, off, slots, wl.k, out=self.out,
-                                 ws=self.fwd_ws, stage_events=events)
+                                 ws=self.fwd_ws, stage_events=events, path=self.flags)
         return off
 
     def active_experts(self) -> int:
@@ -230,8 +232,9 @@ def blas_threads() -> str:
         return "BLAS threads unknown"
 
 
-def workload_report(e4b, torch, wl, steps, warmup, flush=0):
+def workload_report(e4b, torch, wl, steps, warmup, flush=0, flags=0):
     res = Resident(e4b, torch, wl)
+    res.flags = flags
     n_active = res.active_experts()
     m = measure(e4b, torch, res, steps, warmup, flush)
     rl = roofline(wl, n_active, m, load_counters(wl.name + ("" if not flush else "")))
@@ -258,6 +261,8 @@ def main():
     ap.add_argument("--workload", default="mixtral_nf4_prefill", choices=list(WORKLOADS))
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flags", type=lambda v: int(v, 0), default=0,
+                    help="e4b_moe_args.flags for the headline workload (path / tile override)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the layer runs on a "
@@ -272,7 +277,7 @@ def main():
 
     wl = WORKLOADS[args.workload]
     log(f"[bench] device {torch.cuda.get_device_name(0)}; workload {wl.name}")
-    main_rep = workload_report(e4b, torch, wl, args.steps, args.warmup)
+    main_rep = workload_report(e4b, torch, wl, args.steps, args.warmup, flags=args.flags)
     log(f"[bench] {wl.name}: {main_rep['ms_per_step']:.3f} ms/step, {main_rep['tokens_per_s']:.0f} tok/s, "
         f"{main_rep['tflops']:.1f} TFLOP/s, stages {main_rep['stage_ms']}")
 

@@ -21,6 +21,7 @@ __all__ = [
 
 E4B_FMT_NF4, E4B_FMT_MXFP4 = 0, 1
 E4B_PATH_AUTO, E4B_PATH_GEMM, E4B_PATH_GEMV = 0, 1, 2
+E4B_TILE_AUTO, E4B_TILE_32, E4B_TILE_128, E4B_TILE_256 = 0x0, 0x4, 0x8, 0xC
 E4B_ROUTE_RENORMALIZE = 1
 _FMT = {"nf4": E4B_FMT_NF4, "mxfp4": E4B_FMT_MXFP4, E4B_FMT_NF4: E4B_FMT_NF4, E4B_FMT_MXFP4: E4B_FMT_MXFP4}
 

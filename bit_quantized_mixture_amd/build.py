@@ -8,6 +8,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libe4b.so")
 SOURCES = ["abi.hip", "pack.hip", "route.hip", "moe.hip"]
 
@@ -27,7 +28,7 @@ def compile_cmd(out: str) -> list[str]:
         "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-fast-math",
         # keep the compiler from forming packed-fp32 VALU instructions
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wno-unused-command-line-argument",
+        "-Wno-unused-command-line-argument", "-I" + INCLUDE,
         *[os.path.join(CSRC, s) for s in SOURCES],
         "-o", out,
     ]

@@ -3,7 +3,7 @@
 // no alternative code path: on a device other than gfx950 every compute entry point fails.
 #include <string.h>
 
-#include "../../include/e4b.h"
+#include "e4b.h"
 #include "e4b_internal.h"
 
 namespace {
@@ -42,24 +42,35 @@ int check_pack(const void* w, int64_t E, int64_t N, int64_t K, const void* o1, c
   return E4B_OK;
 }
 
-// Row-tile height for the sizes of a forward call (host-known only).
-int pick_bm(const e4b_moe_args* a) {
+// Tile (rows, waves) for the sizes of a forward call (host-known only).
+struct Tile {
+  int bm, waves;
+};
+Tile pick_tile(const e4b_moe_args* a) {
   const int64_t S = a->T * a->k;
   const int path = a->flags & E4B_PATH_MASK;
+  switch (a->flags & E4B_TILE_MASK) {
+    case E4B_TILE_32: return {32, 1};
+    case E4B_TILE_128: return {128, 4};
+    case E4B_TILE_256: return {256, 4};
+    default: break;
+  }
   const double mean_rows = double(S) / double(a->E);
-  if (path == E4B_PATH_GEMV || (path == E4B_PATH_AUTO && mean_rows < 16.0)) return 32;
-  return mean_rows >= 384.0 ? 256 : 128;
+  if (path == E4B_PATH_GEMV || (path == E4B_PATH_AUTO && mean_rows < 16.0)) return {32, 1};
+  return mean_rows >= 512.0 ? Tile{256, 4} : Tile{128, 4};
 }
 
 struct FwdLayout {
-  int bm;
+  int bm, waves;
   int64_t max_mtiles;
   size_t off_x16, off_h, off_y, off_tiles, off_n, total;
 };
 
 int layout_forward(const e4b_moe_args* a, FwdLayout* L) {
   const int64_t S = a->T * a->k;
-  L->bm = pick_bm(a);
+  const Tile t = pick_tile(a);
+  L->bm = t.bm;
+  L->waves = t.waves;
   const int64_t n_active_max = a->E < S ? a->E : S;
   L->max_mtiles = (S + n_active_max * (L->bm - 1)) / L->bm;
   size_t off = 0;
@@ -82,11 +93,15 @@ int check_forward_shape(const e4b_moe_args* a) {
   if (a->fmt != E4B_FMT_NF4 && a->fmt != E4B_FMT_MXFP4) return E4B_ERR_ARG;
   if (a->E <= 0 || a->H <= 0 || a->I <= 0 || a->T < 0 || a->k < 1) return E4B_ERR_ARG;
   if (a->k > a->E) return E4B_ERR_ARG;
-  if ((a->flags & ~E4B_PATH_MASK) != 0 || (a->flags & E4B_PATH_MASK) == 3) return E4B_ERR_ARG;
+  if ((a->flags & ~(E4B_PATH_MASK | E4B_TILE_MASK)) != 0 || (a->flags & E4B_PATH_MASK) == 3)
+    return E4B_ERR_ARG;
   if (a->reserved != 0) return E4B_ERR_ARG;
   if (a->H % 64 || a->I % 64) return E4B_ERR_SHAPE;
   if (a->T * a->k >= (int64_t(1) << 31)) return E4B_ERR_OVERFLOW;
   if (a->E >= (int64_t(1) << 31) || a->H >= (int64_t(1) << 31) || a->I >= (int64_t(1) << 30))
+    return E4B_ERR_OVERFLOW;
+  // activation offsets inside the GEMMs are 32-bit element indices
+  if (a->T * a->H >= (int64_t(1) << 31) || a->T * a->k * a->I >= (int64_t(1) << 31))
     return E4B_ERR_OVERFLOW;
   return E4B_OK;
 }
@@ -191,7 +206,7 @@ int e4b_moe_forward(const e4b_moe_args* a, void* stream) {
   M.T = a->T;
   M.k = a->k;
   M.cfg.bm = L.bm;
-  M.cfg.waves = L.bm == 32 ? 1 : 4;
+  M.cfg.waves = L.waves;
   M.max_mtiles = L.max_mtiles;
   M.x = a->x;
   M.w_gu = a->w_gu;

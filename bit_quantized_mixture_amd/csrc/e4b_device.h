@@ -101,6 +101,16 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
   return b == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(b << 23);
 }
 
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane i's bytes
+// land at lds_wave_base + 16 * i.  lds_wave_base must be the same for the whole wave.  The
+// builtin exists only for the gfx950 device pass; the host pass never runs this body.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_wave_base, 16, 0, 0);
+#endif
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
 // float32 -> bfloat16 bits, round to nearest even (finite inputs).

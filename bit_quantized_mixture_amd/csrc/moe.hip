@@ -19,13 +19,21 @@
 // (v_mfma_f32_32x32x16_f16).  The activation tile (BM x 64 fp16) is staged through LDS,
 // double-buffered, and shared by the waves; each lane streams its own weight row's packed
 // bytes straight from HBM (16 bytes per 64-wide K step) and decodes them in registers.
+#include <type_traits>
+
 #include "e4b_device.h"
 #include "e4b_internal.h"
 
 namespace e4b {
 
-constexpr int kBK = 64;            // K per main-loop step: one NF4 block, two MXFP4 blocks
-constexpr int kPitch = kBK + 8;    // LDS row pitch in fp16 (144 B): conflict-free 16 B reads
+constexpr int kBK = 64;  // K per main-loop step: one NF4 block, two MXFP4 blocks
+
+// LDS activation tile: BM rows x 64 fp16 (128 B), no padding.  The 16-byte chunk holding
+// elements [8c, 8c+8) of row r sits at chunk position c ^ (r & 7) ^ ((r >> 3) & 1).  An MFMA
+// operand read touches one chunk index c in consecutive rows; with 64 four-byte banks a
+// 16-lane phase covers rows r0..r0+15, whose bank groups 8*(r&1) + position are then all
+// distinct (the (r >> 3) term separates rows r and r+8, which share r & 7).
+__device__ __forceinline__ int lds_chunk(int r, int c) { return c ^ (r & 7) ^ ((r >> 3) & 1); }
 
 struct GemmArgs {
   const _Float16* a;       // GU: x16 [T, K]; DN: h [S, K]
@@ -50,13 +58,16 @@ __device__ __forceinline__ int64_t act_pos(int64_t j) {
   return j;
 }
 
+// s_waitcnt immediate: vmcnt = vm (0..63), expcnt = 7 (no wait), lgkmcnt = 0.
+__host__ __device__ constexpr int waitcnt_vm_lgkm0(int vm) {
+  return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4);
+}
+
 template <int FMT, bool GU, int BM, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
-  constexpr int NT = WAVES * 64;
+  constexpr int ST = 4;  // pipeline depth
   constexpr int RB = BM / 32;
-  constexpr int CHUNKS = BM * (kBK / 8) / NT;
-  static_assert(CHUNKS >= 1 && (BM * (kBK / 8)) % NT == 0, "A staging split");
-  __shared__ __attribute__((aligned(16))) _Float16 lds[2][BM][kPitch];
+  __shared__ __attribute__((aligned(16))) _Float16 lds[ST][BM][kBK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
@@ -82,36 +93,55 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
       nrow[f] = n < p.N ? n : p.N - 1;
     }
   }
+  // ---- K order.  K is cut into groups of 256 (4 steps of 64).  Inside group G, step j,
+  // lane half h supplies K elements [256G + 128h + 32j, +32): half h owns a contiguous
+  // 64-byte span of its weight row per group, so the group's four 16-byte loads of a lane
+  // hit the same cache lines back to back, and a group needs one pair of scale loads.  The
+  // activation tile of step j is staged in the same order (chunk c of a row holds K
+  // 256G + 128(c>>2) + 32j + 8(c&3)), so the MFMA k-slots of both operands agree.  The last
+  // group may be partial: out-of-range pieces are loaded from a clamped address and get a
+  // zero scale, so they contribute exactly 0.
   const int64_t kbytes = p.K >> 1;
+  const int nk = int(p.K / kBK);          // real 64-wide steps (= NF4 blocks per row)
+  const int ng = (nk + 3) >> 2;           // 256-wide groups
   const uint8_t* wrow[2];
   const float* srow_nf4[2];
-  const uint8_t* srow_mx[2];
+  const uint16_t* srow_mx[2];
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
     const int64_t r = int64_t(e) * p.N + nrow[f];
-    wrow[f] = p.wq + r * kbytes + 16 * half;
-    srow_nf4[f] = reinterpret_cast<const float*>(p.sc) + r * (p.K >> 6);
-    srow_mx[f] = reinterpret_cast<const uint8_t*>(p.sc) + r * (p.K >> 5) + half;
+    wrow[f] = p.wq + r * kbytes;
+    srow_nf4[f] = reinterpret_cast<const float*>(p.sc) + r * nk;
+    srow_mx[f] = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(p.sc) + r * (2 * nk));
   }
 
-  // ---- activation rows this thread stages (16-byte chunks)
-  const _Float16* arow[CHUNKS];
-  int lrow[CHUNKS], lcol[CHUNKS];
+  // ---- activation staging: global -> LDS directly (global_load_lds_dwordx4).  One
+  // instruction of a wave fills 8 consecutive tile rows (64 lanes x 16 B); lane i writes
+  // LDS chunk position i & 7 of row i >> 3, so it fetches the logical chunk that belongs
+  // there.  Offsets are in fp16 elements from p.a (the ABI keeps them below 2^31).
+  constexpr int ROWS_W = BM / WAVES;      // tile rows staged by this wave
+  constexpr int NLD = ROWS_W / 8;         // DMA instructions per wave per K-step
+  static_assert(ROWS_W % 8 == 0, "DMA row groups");
+  uint32_t arow_off[NLD];                 // row start (elements)
+  uint32_t apart = 0;                     // this lane's chunk offset inside a step (elements)
 #pragma unroll
-  for (int c = 0; c < CHUNKS; ++c) {
-    const int q = tid + c * NT;
-    const int r = q >> 3;
+  for (int j = 0; j < NLD; ++j) {
+    const int r = wave * ROWS_W + 8 * j + (lane >> 3);
     const int rr = r < rows ? r : rows - 1;
-    int64_t src;
-    if (GU) {
-      src = int64_t(p.slots[row0 + rr] / p.k_top);
-    } else {
-      src = int64_t(row0 + rr);
-    }
-    arow[c] = p.a + src * p.K + (q & 7) * 8;
-    lrow[c] = r;
-    lcol[c] = (q & 7) * 8;
+    const int64_t src = GU ? int64_t(p.slots[row0 + rr] / p.k_top) : int64_t(row0 + rr);
+    arow_off[j] = uint32_t(src * p.K);
   }
+  // the logical chunk differs per row only through lds_chunk's row terms; rows of one DMA
+  // instruction are 8*j + (lane >> 3), so (r & 7) = lane >> 3 and (r >> 3) & 1 = parity of
+  // (wave*ROWS_W/8 + j): two variants of the chunk offset per lane.
+  uint32_t apart2[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int c = (lane & 7) ^ (lane >> 3) ^ par;
+    apart2[par] = uint32_t(128 * (c >> 2) + 8 * (c & 3));
+  }
+  (void)apart;
+  const uint32_t kmax_a = uint32_t(p.K - 8);
 
   f32x16 acc[RB][2];
 #pragma unroll
@@ -120,73 +150,167 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
     acc[rb][1] = f32x16{};
   }
 
-  const int nk = int(p.K / kBK);
-  u32x4 areg[CHUNKS];
-  u32x4 breg[2];
-  float sreg[2];
+  // ---- software pipeline.  Step kb (= 4G + j) reads LDS buffer j; the activation DMA of
+  // step kb + ST - 1 is issued at the top of step kb.  Weights and scales of group G + 1
+  // are loaded at the top of group G into the "next" registers.  The step count is padded
+  // to whole groups.
+  const int nk_pad = 4 * ng;
+  u32x4 bg[2][2][4];   // [cur/next][fragment][step in group]
+  // Raw scale words of a half's span (loaded values are only combined where they are used,
+  // so no wait is forced at load time).  NF4: absmax of blocks b0, b0+1 (float bits);
+  // MXFP4: the two 16-bit words holding the e8m0 bytes of 32-blocks b0..b0+3.
+  uint32_t sraw[2][2][2];
+  int gld[2];          // group index loaded into each slot (for validity)
 
-  auto load_a = [&](int kb) {
+  auto stage_a = [&](int kb, int buf) {
+    const uint32_t kg = uint32_t(256 * (kb >> 2) + 32 * (kb & 3));
 #pragma unroll
-    for (int c = 0; c < CHUNKS; ++c) areg[c] = *reinterpret_cast<const u32x4*>(arow[c] + kb * kBK);
+    for (int j = 0; j < NLD; ++j) {
+      const int par = ((wave * ROWS_W) / 8 + j) & 1;
+      uint32_t ko = kg + apart2[par];
+      ko = ko < kmax_a ? ko : kmax_a;
+      lds_dma16(p.a + arow_off[j] + ko, &lds[buf][wave * ROWS_W + 8 * j][0]);
+    }
   };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CHUNKS; ++c)
-      *reinterpret_cast<u32x4*>(&lds[buf][lrow[c]][lcol[c]]) = areg[c];
-  };
-  auto load_b = [&](int kb) {
+  auto load_group = [&](int G, int slot) {
+    gld[slot] = G;
+    const int64_t o0 = int64_t(128) * G + 64 * half;
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
-      breg[f] = *reinterpret_cast<const u32x4*>(wrow[f] + int64_t(kb) * 32);
-      if (FMT == 0)
-        sreg[f] = srow_nf4[f][kb];
-      else
-        sreg[f] = e8m0_to_f32(srow_mx[f][2 * kb]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int64_t o = o0 + 16 * j;
+        o = o < kbytes - 16 ? o : kbytes - 16;
+        bg[slot][f][j] = *reinterpret_cast<const u32x4*>(wrow[f] + o);
+      }
+      if (FMT == 0) {
+        const int b0 = 4 * G + 2 * half;
+        sraw[slot][f][0] = __float_as_uint(srow_nf4[f][b0 < nk ? b0 : nk - 1]);
+        sraw[slot][f][1] = __float_as_uint(srow_nf4[f][b0 + 1 < nk ? b0 + 1 : nk - 1]);
+      } else {
+        const int b0 = 8 * G + 4 * half;  // a row has 2*nk 32-blocks
+        const int i0 = b0 < 2 * nk - 2 ? b0 : 2 * nk - 2;
+        const int i1 = b0 + 2 < 2 * nk - 2 ? b0 + 2 : 2 * nk - 2;
+        sraw[slot][f][0] = srow_mx[f][i0 >> 1];
+        sraw[slot][f][1] = srow_mx[f][i1 >> 1];
+      }
+    }
+  };
+  // Scale of step j of the group in `slot`, fragment f; zero where the step's K range of
+  // this lane's half lies past the end of K.
+  auto step_scale = [&](int slot, int f, int j) -> float {
+    const int G = gld[slot];
+    if (FMT == 0) {
+      const int b = 4 * G + 2 * half + (j >> 1);
+      return b < nk ? __uint_as_float(sraw[slot][f][j >> 1]) : 0.0f;
+    }
+    const int b = 8 * G + 4 * half + j;
+    const uint32_t byte = (sraw[slot][f][j >> 1] >> (8 * (j & 1))) & 0xFFu;
+    return b < 2 * nk ? e8m0_to_f32(byte) : 0.0f;
+  };
+  // Loads per wave: a group issues 2 x (4 weight + 2 scale) loads; a step NLD DMA.
+  constexpr int kGroupOps = 12;
+  auto afrag = [&](int buf, int rb, int s) {
+    const int m = 32 * rb + col;
+    return *reinterpret_cast<const f16x8*>(&lds[buf][m][8 * lds_chunk(m, 4 * half + s)]);
+  };
+
+  // Decoded weight fragments of one 16-wide substep, one substep ahead of their MFMAs.
+  auto decode = [&](const u32x4 (*bsl)[4], int j, int s, float sc0, float sc1, f16x8* out) {
+    const float scs[2] = {sc0, sc1};
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      uint32_t d[4];
+      if (FMT == 0) {
+        nf4_decode8(bsl[f][j][s], d);
+        const f16x2 s16 = f16x2{(_Float16)scs[f], (_Float16)scs[f]};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d[i] = pk_mul_f16(d[i], s16);
+      } else {
+        mxfp4_decode8(bsl[f][j][s], scs[f], d);
+      }
+      out[f] = __builtin_bit_cast(f16x8, u32x4{d[0], d[1], d[2], d[3]});
+    }
+  };
+  constexpr int kMfmaPerSub = 2 * RB;
+  constexpr int kDecodeValu = FMT == 0 ? 58 : 12;
+  constexpr int kValuPerMfma = (kDecodeValu + kMfmaPerSub - 1) / kMfmaPerSub;
+
+  f16x8 afr[RB];
+  f16x8 bcur[2], bnxt[2];
+  // One step: J = position in the group (compile time) = LDS buffer.
+  auto kstep = [&](int G, auto j_c) {
+    constexpr int J = decltype(j_c)::value;
+    constexpr int NXT = (J + ST - 1) % ST;  // buffer freed by the previous step
+    const int kb = 4 * G + J;
+    if (J == 0) load_group(G + 1 < ng ? G + 1 : ng - 1, 1);
+    stage_a(kb + ST - 1, NXT);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s < 3) {
+        decode(bg[0], J, s + 1, step_scale(0, 0, J), step_scale(0, 1, J), bnxt);
+      } else if (J < 3) {
+        decode(bg[0], J + 1, 0, step_scale(0, 0, J + 1), step_scale(0, 1, J + 1), bnxt);
+      } else {
+        decode(bg[1], 0, 0, step_scale(1, 0, 0), step_scale(1, 1, 0), bnxt);
+      }
+      // A fragment rb is reloaded with the next substep's data right after its two MFMAs.
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afr[rb], bcur[0], acc[rb][0], 0, 0, 0);
+        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afr[rb], bcur[1], acc[rb][1], 0, 0, 0);
+        if (s < 3) afr[rb] = afrag(J, rb, s + 1);
+      }
+#pragma unroll
+      for (int i = 0; i < kMfmaPerSub; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);  // VALU
+        if (s < 3 && (i & 1)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      }
+      bcur[0] = bnxt[0];
+      bcur[1] = bnxt[1];
+    }
+    // Step kb+1's DMA (every wave's) has landed; this wave's reads of buffer J are done.
+    // Loads issued after DMA(kb+1): the DMA of steps kb-1 and kb, plus the group loads if
+    // one of those steps opened a group (group loads precede the step's DMA).
+    constexpr int kWait = 2 * NLD + (J < 2 ? kGroupOps : 0);
+    static_assert(kWait < 64, "vmcnt range");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kWait));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) afr[rb] = afrag((J + 1) % ST, rb, 0);
+    if (J == 3) {
+      gld[0] = gld[1];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bg[0][f][q] = bg[1][f][q];
+        sraw[0][f][0] = sraw[1][f][0];
+        sraw[0][f][1] = sraw[1][f][1];
+      }
     }
   };
 
-  load_a(0);
-  load_b(0);
-  store_a(0);
-  __syncthreads();
-
-  for (int kb = 0; kb < nk; ++kb) {
-    const int cur = kb & 1;
-    u32x4 bcur[2] = {breg[0], breg[1]};
-    float scur[2] = {sreg[0], sreg[1]};
-    if (kb + 1 < nk) {
-      load_a(kb + 1);
-      load_b(kb + 1);
-    }
-    f16x2 s16[2];
+  load_group(0, 0);
 #pragma unroll
-    for (int f = 0; f < 2; ++f) s16[f] = f16x2{(_Float16)scur[f], (_Float16)scur[f]};
+  for (int i = 0; i < ST - 1; ++i) stage_a(i, i);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * NLD));  // DMA of step 0 landed
+  __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      f16x8 bfrag[2];
-#pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        uint32_t d[4];
-        if (FMT == 0) {
-          nf4_decode8(bcur[f][s], d);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) d[i] = pk_mul_f16(d[i], s16[f]);
-        } else {
-          mxfp4_decode8(bcur[f][s], scur[f], d);
-        }
-        bfrag[f] = __builtin_bit_cast(f16x8, u32x4{d[0], d[1], d[2], d[3]});
-      }
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const f16x8 afrag =
-            *reinterpret_cast<const f16x8*>(&lds[cur][32 * rb + col][32 * half + 8 * s]);
-        acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afrag, bfrag[0], acc[rb][0], 0, 0, 0);
-        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(afrag, bfrag[1], acc[rb][1], 0, 0, 0);
-      }
-    }
-    if (kb + 1 < nk) store_a(cur ^ 1);
-    __syncthreads();
+  for (int rb = 0; rb < RB; ++rb) afr[rb] = afrag(0, rb, 0);
+  decode(bg[0], 0, 0, step_scale(0, 0, 0), step_scale(0, 1, 0), bcur);
+  for (int G = 0; G < ng; ++G) {
+    kstep(G, std::integral_constant<int, 0>{});
+    kstep(G, std::integral_constant<int, 1>{});
+    kstep(G, std::integral_constant<int, 2>{});
+    kstep(G, std::integral_constant<int, 3>{});
   }
+  (void)nk_pad;
+  // drain the DMA issued past the last step before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
   // ---- epilogue.  Accumulator element r of a 32x32 block: row 8*(r/4) + 4*half + r%4,
   // column = col.
@@ -226,6 +350,17 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
     }
   }
 }
+
+// Explicit instantiations: the host pass does not emit launch stubs for these templates
+// implicitly (their bodies use generic lambdas).
+#define E4B_GEMM_INST(FMT, GU, BM, W) \
+  template __global__ void moe_gemm_kernel<FMT, GU, BM, W>(GemmArgs);
+#define E4B_GEMM_INST_ALL(FMT)                                                           \
+  E4B_GEMM_INST(FMT, true, 256, 4) E4B_GEMM_INST(FMT, false, 256, 4)                     \
+  E4B_GEMM_INST(FMT, true, 128, 4) E4B_GEMM_INST(FMT, false, 128, 4)                     \
+  E4B_GEMM_INST(FMT, true, 32, 1) E4B_GEMM_INST(FMT, false, 32, 1)
+E4B_GEMM_INST_ALL(0)
+E4B_GEMM_INST_ALL(1)
 
 // x bf16 -> fp16 (exact for |x| in fp16's normal range), stored in the k-slot order of the
 // weight format inside each aligned group of 8.

@@ -66,6 +66,13 @@ typedef enum e4b_fmt { E4B_FMT_NF4 = 0, E4B_FMT_MXFP4 = 1 } e4b_fmt;
 #define E4B_PATH_GEMM 0x1 /* MFMA grouped GEMM, 256-row tiles */
 #define E4B_PATH_GEMV 0x2 /* small-M streaming path, 32-row tiles */
 #define E4B_PATH_MASK 0x3
+/* e4b_moe_args.flags bits 2-3: row-tile override for the MFMA path (0 = chosen from the
+ * sizes): 32 rows (1 wave), 128 rows (4 waves), 256 rows (4 waves). */
+#define E4B_TILE_AUTO 0x0
+#define E4B_TILE_32 0x4
+#define E4B_TILE_128 0x8
+#define E4B_TILE_256 0xC
+#define E4B_TILE_MASK 0xC
 
 /*
  * e4b_pack_nf4 — quantise bf16 expert stacks to NF4.
@@ -134,7 +141,7 @@ typedef struct e4b_moe_args {
   float* out_f32;         /* [T, H] float32 out, or NULL: the value `out` is rounded from */
   void* ws;               /* device workspace of at least e4b_moe_workspace_bytes() */
   size_t ws_bytes;
-  int32_t flags;          /* E4B_PATH_* */
+  int32_t flags;          /* E4B_PATH_* | E4B_TILE_* */
   int32_t reserved;       /* must be 0 */
   /* NULL, or 6 hipEvent_t the call records on `stream` around its 5 stages (x conversion,
    * tile map, gate_up GEMM, down GEMM, combine), so a caller can time each kernel on the

@@ -102,7 +102,8 @@ def test_forward_rejects_bad_arguments(e4b):
     assert f(E=0) == ERR_ARG
     assert f(T=-1) == ERR_ARG
     assert f(flags=3) == ERR_ARG
-    assert f(flags=4) == ERR_ARG
+    assert f(flags=0x10) == ERR_ARG
+    assert f(flags=7) == ERR_ARG
     assert f(H=96) == ERR_SHAPE
     assert f(I=100) == ERR_SHAPE
     assert f(x=None) == ERR_ARG
@@ -112,6 +113,7 @@ def test_forward_rejects_bad_arguments(e4b):
     assert f(out_f32=FAKE + 4) == ERR_ALIGN
     assert f(ws_bytes=1024) == ERR_WORKSPACE
     assert f(T=1 << 28, k=8) == ERR_OVERFLOW
+    assert f(T=1 << 20, H=1 << 12) == ERR_OVERFLOW
 
 
 def test_workspace_sizes_cover_the_intermediates(e4b):
