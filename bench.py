@@ -3,13 +3,15 @@
 
 One step = one pass of the whole hot path over one batch: e4b_route_permute (top-k, softmax
 weights, expert-major slot order) followed by e4b_moe_forward (x conversion, tile map,
-grouped gate_up GEMM + SwiGLU, grouped down GEMM + routing weight, combine) on weights that
-are already packed and resident in HBM.  Inputs are the seeded synthetic tensors of
+grouped gate_up GEMM + SwiGLU, grouped down GEMM, weighted combine) on weights that are
+already packed and resident in HBM.  Inputs are the seeded synthetic tensors of
 moe_inputs.py.  Prints ONE JSON line on stdout; progress goes to stderr.
 
 The headline workload is the Mixtral-shaped NF4 prefill layer (E=8, H=4096, I=14336, top-2,
-T=4096).  The same line carries, under "secondary", the skewed 64-expert prefill layer and
-the 128-expert decode layer (T=64 and T=1), and a float64 CPU-oracle baseline timed on a
+T=4096).  The same line carries, under "secondary", the skewed 64-expert prefill layer, the
+MXFP4 layer and the 128-expert decode layer at T = 64, 16, 4, 1 (warm, and cold with the
+256 MB Infinity Cache flushed before every step; eager launches with per-stage HIP events,
+and the same step replayed from a HIP graph), and a float64 CPU-oracle baseline timed on a
 bounded sample of the headline workload.
 """
 from __future__ import annotations
@@ -31,6 +33,7 @@ from moe_inputs import WORKLOADS, make_expert_weight, make_logits, make_x  # noq
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD published
 PEAK_F16_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, AMD published
 STAGES = ["convert_x", "build_tiles", "gemm_gate_up", "gemm_down", "combine"]
+MALL_FLUSH_BYTES = 1 << 30     # > 256 MB Infinity Cache
 
 
 def log(*a):
@@ -41,15 +44,13 @@ def bytes_per_weight(fmt: str) -> float:
     return 0.5 + (4.0 / 64 if fmt == "nf4" else 1.0 / 32)
 
 
-class Resident:
-    """Packed weights, x and logits of one workload, resident on the GPU."""
+class Layer:
+    """Packed weights of one workload, resident on the GPU (packed there by the library)."""
 
     def __init__(self, e4b, torch, wl):
         self.e4b, self.torch, self.wl = e4b, torch, wl
         dev = "cuda:0"
         t0 = time.time()
-        self.x = torch.from_numpy(make_x(wl).view(np.int16)).to(dev).view(torch.bfloat16)
-        self.logits = torch.from_numpy(make_logits(wl)).to(dev)
         self.packed = {}
         self.pack_s = 0.0
         for which, (N, K) in (("gate_up", (2 * wl.I, wl.H)), ("down", (wl.H, wl.I))):
@@ -68,21 +69,37 @@ class Resident:
             self.pack_s += a.elapsed_time(b) / 1e3
             del w
         self.pack_bytes = wl.E * 3 * wl.H * wl.I * (2 + bytes_per_weight(wl.fmt))  # bf16 in, codes+scales out
-        self.route_ws = torch.empty(max(256, e4b.e4b_route_workspace_bytes(wl.T, wl.E, wl.k)),
-                                    dtype=torch.uint8, device=dev)
-        self.fwd_ws = torch.empty(e4b.e4b_moe_workspace_bytes(wl.fmt, wl.E, wl.H, wl.I, wl.T, wl.k),
-                                  dtype=torch.uint8, device=dev)
-        self.out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device=dev)
         torch.cuda.synchronize()
-        log(f"[bench] {wl.name}: resident in {time.time() - t0:.1f}s (pack {self.pack_s * 1e3:.1f} ms)")
+        log(f"[bench] {wl.name}: weights resident in {time.time() - t0:.1f}s (GPU pack {self.pack_s * 1e3:.1f} ms)")
+
+
+class Batch:
+    """x, router logits and every output / workspace buffer of one batch size."""
 
     flags = 0
 
+    def __init__(self, layer: Layer, T: int):
+        torch, e4b = layer.torch, layer.e4b
+        self.layer, self.e4b = layer, e4b
+        self.wl = wl = layer.wl.with_T(T)
+        dev = "cuda:0"
+        self.x = torch.from_numpy(make_x(wl).view(np.int16)).to(dev).view(torch.bfloat16)
+        self.logits = torch.from_numpy(make_logits(wl)).to(dev)
+        self.route_out = (torch.empty((T, wl.k), dtype=torch.int32, device=dev),
+                          torch.empty((T, wl.k), dtype=torch.float32, device=dev),
+                          torch.empty((wl.E + 1,), dtype=torch.int32, device=dev),
+                          torch.empty((T * wl.k,), dtype=torch.int32, device=dev))
+        self.route_ws = torch.empty(max(256, e4b.e4b_route_workspace_bytes(T, wl.E, wl.k)),
+                                    dtype=torch.uint8, device=dev)
+        self.fwd_ws = torch.empty(max(256, e4b.e4b_moe_workspace_bytes(wl.fmt, wl.E, wl.H, wl.I, T, wl.k)),
+                                  dtype=torch.uint8, device=dev)
+        self.out = torch.empty((T, wl.H), dtype=torch.bfloat16, device=dev)
+
     def step(self, events=None):
         wl = self.wl
-        ids, w, off, slots = self.e4b.e4b_route_permute(self.logits, wl.k, ws=self.route_ws)
-        gp, gs = self.packed["gate_up"]
-        dp, ds = self.packed["down"]
+        ids, w, off, slots = self.e4b.e4b_route_permute(self.logits, wl.k, ws=self.route_ws, out=self.route_out)
+        gp, gs = self.layer.packed["gate_up"]
+        dp, ds = self.layer.packed["down"]
         self.e4b.e4b_moe_forward(wl.fmt, self.x, gp, gs, dp, ds, w, off, slots, wl.k, out=self.out,
                                  ws=self.fwd_ws, stage_events=events, path=self.flags)
         return off
@@ -92,14 +109,13 @@ class Resident:
         return int(np.count_nonzero(np.diff(off)))
 
 
-def measure(e4b, torch, res: Resident, steps: int, warmup: int, flush_bytes: int = 0):
+def measure(torch, b: Batch, steps: int, warmup: int, flush_bytes: int = 0):
     """Time `steps` route+forward steps.  Per-stage kernel times come from HIP events the
     library records on the stream it launches on.  With flush_bytes > 0, a buffer of that
     size is overwritten before each step (outside the events) so weights come from HBM."""
-    wl = res.wl
     flush = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda:0") if flush_bytes else None
     for _ in range(warmup):
-        res.step()
+        b.step()
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     for row in ev:
@@ -115,13 +131,13 @@ def measure(e4b, torch, res: Resident, steps: int, warmup: int, flush_bytes: int
         if flush is not None:
             flush.fill_(i & 0xFF)
         step_ev[i][0].record()
-        res.step(ev[i])
+        b.step(ev[i])
         step_ev[i][1].record()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     stage_ms = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(5)] for i in range(steps)])
-    step_ms = np.array([a.elapsed_time(b) for a, b in step_ev])
+    step_ms = np.array([a.elapsed_time(c) for a, c in step_ev])
     total_ms = t_begin.elapsed_time(t_end)
     return {
         "ms_per_step": float(total_ms / steps) if flush is None else float(np.mean(step_ms)),
@@ -133,8 +149,36 @@ def measure(e4b, torch, res: Resident, steps: int, warmup: int, flush_bytes: int
     }
 
 
+def measure_graph(torch, b: Batch, steps: int):
+    """The same step captured once into a HIP graph and replayed `steps` times back to back
+    (no per-stage events): the step's GPU time without host launch gaps."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            b.step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        b.step()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    a, c = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        g.replay()
+    c.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(c) / steps
+    del g
+    return ms
+
+
 def roofline(wl, n_active: int, m: dict, counters: dict | None):
-    """Roofline entry for the dominant kernel of the step."""
+    """Roofline entry for the dominant kernel of the step (algorithmic work per launch over
+    its mean launch time from the HIP events)."""
     S = wl.T * wl.k
     bw = bytes_per_weight(wl.fmt)
     stage = max(("gemm_gate_up", "gemm_down"), key=lambda s: m["stage_ms"][s])
@@ -146,7 +190,7 @@ def roofline(wl, n_active: int, m: dict, counters: dict | None):
     else:
         flops = 2.0 * wl.H * wl.I * S
         wbytes = n_active * wl.H * wl.I * bw
-        abytes = 2.0 * S * wl.I + 4.0 * S * wl.H              # h read, weighted y written
+        abytes = 2.0 * S * wl.I + 4.0 * S * wl.H              # h read, y (fp32) written
     mean_rows = S / wl.E
     if mean_rows < 16:  # bandwidth-bound small-M streaming
         achieved = (wbytes + abytes) / t / 1e9
@@ -156,27 +200,28 @@ def roofline(wl, n_active: int, m: dict, counters: dict | None):
         achieved = flops / t / 1e12
         entry = {"bound": "mfma", "achieved": achieved, "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
                  "frac": achieved / PEAK_F16_MFMA_TFLOPS}
+    entry["traffic"] = None
+    if counters and counters.get(stage):
+        entry["traffic"] = counters[stage]
     entry["kernel"] = stage
     entry["kernel_ms"] = m["stage_ms"][stage]
     entry["algorithmic_bytes"] = wbytes + abytes
     entry["algorithmic_flops"] = flops
-    entry["traffic"] = None
-    if counters and counters.get(stage):
-        entry["traffic"] = counters[stage]
     return entry
 
 
 def kernel_source_sha() -> str:
     h = hashlib.sha256()
-    for f in ("moe.hip", "e4b_device.h"):
+    for f in ("moe.hip", "gemv.hip", "e4b_device.h"):
         with open(os.path.join(ROOT, "bit_quantized_mixture_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def load_counters(workload: str) -> dict:
-    """HBM traffic per launch measured with rocprofv3 counters (profiles/hbm_traffic.txt),
-    used only if the kernel sources are unchanged since the counters were taken."""
+    """HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (profiles/hbm_traffic.txt,
+    already scaled by the copy-kernel calibration), used only while the kernel sources are
+    the ones the counters were taken on."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
     out = {}
     if not os.path.exists(path):
@@ -190,37 +235,48 @@ def load_counters(workload: str) -> dict:
     return out
 
 
-def cpu_baseline(wl, threads_note: str):
+def cpu_baseline(wl, threads_note: str, min_s: float = 12.0, max_reps: int = 40):
     """The float64 oracle on a bounded sample of the workload: the rows routed to expert 0.
-    Timed: oracle routing of all T tokens, decode of expert 0's gate_up and down slices,
-    the float64 SwiGLU MLP on its rows and their weighted accumulation.  Scaled to tokens/s
-    as (rows of expert 0 / k) / time, i.e. the rate at which the whole layer would run if
-    every expert cost the same."""
+    Packing expert 0's two weight slices with the oracle is timed on its own (elements/s).
+    The forward sample -- oracle routing of all T tokens, decode of expert 0's gate_up and
+    down slices, the float64 SwiGLU MLP on its rows and their weighted accumulation -- is
+    repeated until it has run at least `min_s` seconds, and scaled to tokens/s as
+    (rows of expert 0 / k) * repetitions / time, i.e. the rate at which the whole layer would
+    run if every expert cost the same."""
     from oracle import moe as omoe
     from oracle import mxfp4 as omx
     from oracle import nf4 as onf4
     from oracle import route as oroute
     q = onf4 if wl.fmt == "nf4" else omx
-    gp, gs = q.quantize_pack(make_expert_weight(wl, "gate_up", 0)[None])
-    dp, ds = q.quantize_pack(make_expert_weight(wl, "down", 0)[None])
+    g_bits, d_bits = make_expert_weight(wl, "gate_up", 0), make_expert_weight(wl, "down", 0)
+    t0 = time.perf_counter()
+    gp, gs = q.quantize_pack(g_bits[None])
+    dp, ds = q.quantize_pack(d_bits[None])
+    pack_s = time.perf_counter() - t0
     x_bits = make_x(wl)
     logits = make_logits(wl)
+    reps, rows = 0, 0
     t0 = time.perf_counter()
-    ids, w, counts, offsets, slots = oroute.route(logits, wl.k)
-    seg = slots[offsets[0]:offsets[1]]
-    tok, j = seg // wl.k, seg % wl.k
-    x = omoe.bf16_bits_to_f64(x_bits[tok])
-    y = omoe.expert_mlp(x, omoe.decode_expert(wl.fmt, gp, gs, 0), omoe.decode_expert(wl.fmt, dp, ds, 0))
-    out = np.zeros((wl.T, wl.H))
-    np.add.at(out, tok, w[tok, j][:, None] * y)
+    while reps < max_reps and (reps == 0 or time.perf_counter() - t0 < min_s):
+        ids, w, counts, offsets, slots = oroute.route(logits, wl.k)
+        seg = slots[offsets[0]:offsets[1]]
+        tok, j = seg // wl.k, seg % wl.k
+        x = omoe.bf16_bits_to_f64(x_bits[tok])
+        y = omoe.expert_mlp(x, omoe.decode_expert(wl.fmt, gp, gs, 0), omoe.decode_expert(wl.fmt, dp, ds, 0))
+        out = np.zeros((wl.T, wl.H))
+        np.add.at(out, tok, w[tok, j][:, None] * y)
+        rows = len(seg)
+        reps += 1
     dt = time.perf_counter() - t0
-    rows = len(seg)
-    return {"value": (rows / wl.k) / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+    n_el = g_bits.size + d_bits.size
+    return {"value": (rows / wl.k) * reps / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
             "kind": "oracle",
             "sample": f"{wl.name}: the {rows} rows routed to expert 0 (of {wl.T * wl.k}); oracle routing of "
-                      f"all {wl.T} tokens + decode of expert 0 + float64 SwiGLU MLP + weighted accumulate; "
-                      f"{dt:.1f} s; {threads_note}",
-            "seconds": dt}
+                      f"all {wl.T} tokens + decode of expert 0 + float64 SwiGLU MLP + weighted accumulate, "
+                      f"{reps} repetitions in {dt:.1f} s; {threads_note}",
+            "seconds": dt,
+            "pack_elements_per_s": n_el / pack_s,
+            "pack_sample": f"oracle {wl.fmt} packing of expert 0's gate_up and down ({n_el} elements) in {pack_s:.1f} s"}
 
 
 def blas_threads() -> str:
@@ -232,12 +288,14 @@ def blas_threads() -> str:
         return "BLAS threads unknown"
 
 
-def workload_report(e4b, torch, wl, steps, warmup, flush=0, flags=0):
-    res = Resident(e4b, torch, wl)
-    res.flags = flags
-    n_active = res.active_experts()
-    m = measure(e4b, torch, res, steps, warmup, flush)
-    rl = roofline(wl, n_active, m, load_counters(wl.name + ("" if not flush else "")))
+def batch_report(torch, layer: Layer, T: int, steps: int, warmup: int, flush: int = 0, flags: int = 0,
+                 graph: bool = False):
+    b = Batch(layer, T)
+    b.flags = flags
+    wl = b.wl
+    n_active = b.active_experts()
+    m = measure(torch, b, steps, warmup, flush)
+    rl = roofline(wl, n_active, m, None if flush else load_counters(wl.name))
     S = wl.T * wl.k
     ms = m["ms_per_step"]
     rep = {
@@ -245,12 +303,24 @@ def workload_report(e4b, torch, wl, steps, warmup, flush=0, flags=0):
         "step_ms_median": m["step_ms_median"], "step_ms_p10": m["step_ms_p10"], "step_ms_p90": m["step_ms_p90"],
         "tflops": 6.0 * wl.H * wl.I * S / (ms / 1e3) / 1e12, "active_experts": n_active,
         "stage_ms": m["stage_ms"], "roofline": rl,
-        "pack_gbs": res.pack_bytes / res.pack_s / 1e9,
         "mall_flushed": bool(flush),
     }
-    del res
+    if graph:
+        gms = measure_graph(torch, b, max(steps, 50))
+        rep["graph_ms_per_step"] = gms
+        rep["graph_tokens_per_s"] = wl.T / (gms / 1e3)
+    del b
     torch.cuda.empty_cache()
     return rep
+
+
+def fmt_rep(key, rep):
+    rl = rep["roofline"]
+    s = (f"[bench] {key}: {rep['ms_per_step']:.4f} ms/step, {rep['tokens_per_s']:.0f} tok/s, "
+         f"{rl['kernel']} {rl['achieved']:.1f} {rl['unit']} ({100 * rl['frac']:.1f}% of peak)")
+    if "graph_ms_per_step" in rep:
+        s += f", graph {rep['graph_ms_per_step']:.4f} ms/step"
+    return s
 
 
 def main():
@@ -277,32 +347,40 @@ def main():
 
     wl = WORKLOADS[args.workload]
     log(f"[bench] device {torch.cuda.get_device_name(0)}; workload {wl.name}")
-    main_rep = workload_report(e4b, torch, wl, args.steps, args.warmup, flags=args.flags)
-    log(f"[bench] {wl.name}: {main_rep['ms_per_step']:.3f} ms/step, {main_rep['tokens_per_s']:.0f} tok/s, "
-        f"{main_rep['tflops']:.1f} TFLOP/s, stages {main_rep['stage_ms']}")
+    layer = Layer(e4b, torch, wl)
+    pack_gbs = layer.pack_bytes / layer.pack_s / 1e9
+    main_rep = batch_report(torch, layer, wl.T, args.steps, args.warmup, flags=args.flags)
+    log(fmt_rep(wl.name, main_rep) + f"; stages {main_rep['stage_ms']}")
+    del layer
+    torch.cuda.empty_cache()
 
     secondary = {}
     if not args.no_secondary:
-        for name, T, flush in (("skewed_nf4_prefill", None, 0), ("mxfp4_moe", None, 0),
-                               ("finegrained_nf4_decode", 64, 0), ("finegrained_nf4_decode", 64, 1 << 30),
-                               ("finegrained_nf4_decode", 1, 0), ("finegrained_nf4_decode", 1, 1 << 30)):
-            if name == wl.name and T is None:
+        for name in ("skewed_nf4_prefill", "mxfp4_moe"):
+            if name == wl.name:
                 continue
-            swl = WORKLOADS[name] if T is None else WORKLOADS[name].with_T(T)
-            key = swl.name + ("" if T is None else f"_T{T}") + ("_cold" if flush else "")
-            rep = workload_report(e4b, torch, swl, max(args.steps, 20), args.warmup, flush)
-            secondary[key] = rep
-            log(f"[bench] {key}: {rep['ms_per_step']:.4f} ms/step, {rep['tokens_per_s']:.0f} tok/s, "
-                f"roofline {rep['roofline']['kernel']} {rep['roofline']['achieved']:.1f} "
-                f"{rep['roofline']['unit']} ({100 * rep['roofline']['frac']:.1f}%)")
+            lay = Layer(e4b, torch, WORKLOADS[name])
+            secondary[name] = batch_report(torch, lay, WORKLOADS[name].T, max(args.steps, 10), args.warmup)
+            log(fmt_rep(name, secondary[name]))
+            del lay
+            torch.cuda.empty_cache()
+        dwl = WORKLOADS["finegrained_nf4_decode"]
+        lay = Layer(e4b, torch, dwl)
+        for T, flush in ((64, 0), (16, 0), (4, 0), (1, 0), (64, MALL_FLUSH_BYTES), (1, MALL_FLUSH_BYTES)):
+            key = f"{dwl.name}_T{T}" + ("_cold" if flush else "")
+            secondary[key] = batch_report(torch, lay, T, max(args.steps, 50), args.warmup, flush,
+                                          graph=not flush)
+            log(fmt_rep(key, secondary[key]))
+        del lay
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
         cpu = cpu_baseline(wl, blas_threads())
-        log(f"[bench] cpu baseline {cpu['value']:.1f} tokens/s in {cpu['seconds']:.1f}s")
+        log(f"[bench] cpu baseline {cpu['value']:.1f} tokens/s over {cpu['seconds']:.1f}s; "
+            f"oracle pack {cpu['pack_elements_per_s'] / 1e6:.1f} M elements/s")
 
-    rl = dict(main_rep["roofline"])
     line = {
         "metric": "MoE layer tokens/s + achieved HBM GB/s / MFMA TFLOP/s vs MI355X peak",
         "value": main_rep["tokens_per_s"],
@@ -320,8 +398,9 @@ def main():
                    "T": wl.T, "global_batch": wl.T, "parallelism": "single GPU"},
         "tflops": main_rep["tflops"],
         "stage_ms": main_rep["stage_ms"],
-        "roofline": rl,
+        "roofline": dict(main_rep["roofline"]),
         "cpu_baseline": cpu,
+        "gpu_pack_gbs": pack_gbs,
         "secondary": secondary,
         "kernel_source_sha": kernel_source_sha(),
     }

@@ -141,18 +141,25 @@ def e4b_route_workspace_bytes(T: int, E: int, k: int) -> int:
     return n.value
 
 
-def e4b_route_permute(logits, k: int, renormalize: bool = True, ws=None, stream=None):
+def e4b_route_permute(logits, k: int, renormalize: bool = True, ws=None, stream=None, out=None):
     """logits [T, E] float32 -> (topk_ids [T,k] i32, topk_w [T,k] f32, expert_offsets [E+1] i32,
-    sorted_slots [T*k] i32)."""
+    sorted_slots [T*k] i32).  `out`: optional preallocated (ids, w, offsets, slots)."""
     _need(logits, "logits", (torch.float32,))
     T, E = logits.shape
     dev = logits.device
-    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-    w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
-    slots = torch.empty((T * k,), dtype=torch.int32, device=dev)
-    need = e4b_route_workspace_bytes(T, E, k)
+    if out is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+        slots = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    else:
+        ids, w, offsets, slots = out
+        _need(ids, "topk_ids", (torch.int32,), (T, k))
+        _need(w, "topk_w", (torch.float32,), (T, k))
+        _need(offsets, "expert_offsets", (torch.int32,), (E + 1,))
+        _need(slots, "sorted_slots", (torch.int32,), (T * k,))
     if ws is None:
+        need = e4b_route_workspace_bytes(T, E, k)
         ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
     flags = E4B_ROUTE_RENORMALIZE if renormalize else 0
     _check("e4b_route_permute", _c_route(

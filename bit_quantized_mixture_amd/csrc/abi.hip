@@ -44,26 +44,27 @@ int check_pack(const void* w, int64_t E, int64_t N, int64_t K, const void* o1, c
 
 // Tile (rows, waves) for the sizes of a forward call (host-known only).
 struct Tile {
-  int bm, waves;
+  int bm, waves, gemv;
 };
 Tile pick_tile(const e4b_moe_args* a) {
   const int64_t S = a->T * a->k;
   const int path = a->flags & E4B_PATH_MASK;
   switch (a->flags & E4B_TILE_MASK) {
-    case E4B_TILE_32: return {32, 1};
-    case E4B_TILE_128: return {128, 4};
-    case E4B_TILE_256: return {256, 4};
+    case E4B_TILE_32: return {32, 1, 0};
+    case E4B_TILE_128: return {128, 4, 0};
+    case E4B_TILE_256: return {256, 4, 0};
     default: break;
   }
   const double mean_rows = double(S) / double(a->E);
-  if (path == E4B_PATH_GEMV || (path == E4B_PATH_AUTO && mean_rows < 16.0)) return {32, 1};
-  return mean_rows >= 512.0 ? Tile{256, 4} : Tile{128, 4};
+  if (path == E4B_PATH_GEMV || (path == E4B_PATH_AUTO && mean_rows < 16.0))
+    return {e4b::kGemvTileRows, 4, 1};
+  return mean_rows >= 512.0 ? Tile{256, 4, 0} : Tile{128, 4, 0};
 }
 
 struct FwdLayout {
-  int bm, waves;
+  int bm, waves, gemv;
   int64_t max_mtiles;
-  size_t off_x16, off_h, off_y, off_tiles, off_n, total;
+  size_t off_x16, off_h, off_y, off_inv, off_tiles, off_n, total;
 };
 
 int layout_forward(const e4b_moe_args* a, FwdLayout* L) {
@@ -71,6 +72,7 @@ int layout_forward(const e4b_moe_args* a, FwdLayout* L) {
   const Tile t = pick_tile(a);
   L->bm = t.bm;
   L->waves = t.waves;
+  L->gemv = t.gemv;
   const int64_t n_active_max = a->E < S ? a->E : S;
   L->max_mtiles = (S + n_active_max * (L->bm - 1)) / L->bm;
   size_t off = 0;
@@ -80,6 +82,8 @@ int layout_forward(const e4b_moe_args* a, FwdLayout* L) {
   off += align_up(size_t(S) * size_t(a->I) * 2);
   L->off_y = off;
   off += align_up(size_t(S) * size_t(a->H) * 4);
+  L->off_inv = off;
+  off += align_up(size_t(S) * 4);
   L->off_tiles = off;
   off += align_up(size_t(L->max_mtiles) * 16);
   L->off_n = off;
@@ -94,6 +98,9 @@ int check_forward_shape(const e4b_moe_args* a) {
   if (a->E <= 0 || a->H <= 0 || a->I <= 0 || a->T < 0 || a->k < 1) return E4B_ERR_ARG;
   if (a->k > a->E) return E4B_ERR_ARG;
   if ((a->flags & ~(E4B_PATH_MASK | E4B_TILE_MASK)) != 0 || (a->flags & E4B_PATH_MASK) == 3)
+    return E4B_ERR_ARG;
+  // a row-tile override names an MFMA tile; it cannot go with the streaming path
+  if ((a->flags & E4B_PATH_MASK) == E4B_PATH_GEMV && (a->flags & E4B_TILE_MASK) != 0)
     return E4B_ERR_ARG;
   if (a->reserved != 0) return E4B_ERR_ARG;
   if (a->H % 64 || a->I % 64) return E4B_ERR_SHAPE;
@@ -207,6 +214,7 @@ int e4b_moe_forward(const e4b_moe_args* a, void* stream) {
   M.k = a->k;
   M.cfg.bm = L.bm;
   M.cfg.waves = L.waves;
+  M.cfg.gemv = L.gemv;
   M.max_mtiles = L.max_mtiles;
   M.x = a->x;
   M.w_gu = a->w_gu;
@@ -221,6 +229,7 @@ int e4b_moe_forward(const e4b_moe_args* a, void* stream) {
   M.x16 = reinterpret_cast<_Float16*>(ws + L.off_x16);
   M.h = reinterpret_cast<_Float16*>(ws + L.off_h);
   M.y = reinterpret_cast<float*>(ws + L.off_y);
+  M.inv = reinterpret_cast<int32_t*>(ws + L.off_inv);
   M.tiles = reinterpret_cast<int32_t*>(ws + L.off_tiles);
   M.n_mtiles = reinterpret_cast<int32_t*>(ws + L.off_n);
   M.events = a->stage_events;

@@ -53,6 +53,14 @@ __device__ __constant__ const uint32_t kNf4Up[15] = {
 // Inverse (element e lives in slot kNf4ElemSlot[e]): 0 4 1 5 2 6 3 7.
 __host__ __device__ constexpr int nf4_elem_slot(int e) { return (e >> 1) | ((e & 1) << 2); }
 
+// Position of activation column j inside its row, in the k-slot order of the weight
+// format (NF4 decodes 8 elements in slot order, MXFP4 in natural order).
+template <int FMT>
+__device__ __forceinline__ int64_t act_pos(int64_t j) {
+  if (FMT == 0) return (j & ~int64_t(7)) | nf4_elem_slot(int(j & 7));
+  return j;
+}
+
 __device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) {
   return __builtin_amdgcn_perm(s0, s1, sel);
 }
@@ -111,7 +119,18 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds_wave_base) 
 #endif
 }
 
+// s_waitcnt immediate: vmcnt = vm (0..63), expcnt = 7 (no wait), lgkmcnt = 0.
+__host__ __device__ constexpr int waitcnt_vm_lgkm0(int vm) {
+  return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// SiLU(g) * u in fp32 with the hardware exp and reciprocal (the result is stored as fp16).
+// For very negative g, exp(-g) overflows to inf and the reciprocal gives 0 (SiLU -> -0).
+__device__ __forceinline__ float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 // float32 -> bfloat16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {

@@ -9,10 +9,15 @@ namespace e4b {
 // Tile shapes of the grouped expert GEMM.  BM = rows (routed slots) per tile; the N extent
 // per workgroup is 32 h-columns per wave for gate_up (a 32-wide gate fragment and the
 // matching 32-wide up fragment) and 64 output columns per wave for down.
+// gemv = 1 selects the small-M streaming kernels (gemv.hip) instead, with tiles of at most
+// kGemvTileRows rows.
 struct TileCfg {
   int bm;
   int waves;
+  int gemv;
 };
+
+constexpr int kGemvTileRows = 16;
 
 hipError_t launch_pack_nf4(const uint16_t* w, int64_t n_elems, uint8_t* packed, float* absmax,
                            hipStream_t stream);
@@ -43,12 +48,16 @@ struct MoeLaunch {
   // workspace carve-outs
   _Float16* x16;   // [T, H]
   _Float16* h;     // [S, I]
-  float* y;        // [S, H]
+  float* y;        // [S, H], sorted-row order
+  int32_t* inv;    // [S]: slot -> sorted row
   int32_t* tiles;  // [max_mtiles, 4]
   int32_t* n_mtiles;
   void* const* events;  // nullable: 6 hipEvent_t around the 5 stages
 };
 
 hipError_t launch_moe_forward(const MoeLaunch& L, hipStream_t stream);
+
+// Small-M streaming kernels: stage 0 = gate_up + SwiGLU (x16 -> h), 1 = down (h -> y).
+hipError_t launch_gemv(const MoeLaunch& L, hipStream_t stream, int stage);
 
 }  // namespace e4b

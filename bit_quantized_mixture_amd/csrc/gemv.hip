@@ -1,0 +1,453 @@
+// Small-M expert path (decode): the same grouped gate_up + SwiGLU and down products as
+// moe.hip, shaped for experts that receive only a few routed rows.  There the work is
+// streaming the packed weights once (grouped-nf4-gemm 0.25.0 project description: the decode
+// GEMV beside the grouped GEMM), so this kernel is built around HBM throughput:
+//
+// * Persistent workgroups of 4 waves, two per CU.  A work item is (tile of <= 16 routed rows
+//   of one expert, block of 64 * RB weight rows); each wave owns RB row blocks of 16 rows.  A
+//   workgroup walks its items and, inside each item, K in steps of 256, as one flat sequence.
+// * 16x16x32 f16 MFMA with the weights as the A operand and the routed activations as B (16
+//   columns): D[row, token] += sum_k W[row, k] * X[token, k].  One activation fragment read
+//   from LDS feeds the RB row blocks of the wave.
+// * Software pipeline: while step s is computed, the weights, scales and activations of step
+//   s + 1 are in flight in registers.  Every wave issues the same number of memory operations
+//   in every step, with no branch around them (past the last step the loads repeat it and are
+//   not used), so one s_waitcnt per step covers it and the compiler's own counting agrees.
+//   The activations of step s go to LDS (double buffer) with ordinary ds_write once they have
+//   landed: a direct global->LDS copy in flight during the compute would make the compiler
+//   wait for every LDS read to drain (lgkmcnt(0)).
+// * NF4 decode through a 256-entry LDS table of fp16 pairs, one per packed byte value, with a
+//   private copy for each lane: lane l's copy sits entirely in LDS bank l, so the 64 lookups of
+//   a wave never conflict, and one v_perm builds each lookup address (byte value * 256 + lane
+//   * 4).  A packed dword costs 4 v_perm + 4 ds_read_b32 + 4 v_pk_mul_f16 (the scale), against
+//   ~28 VALU operations for an in-register table.  MXFP4 uses the hardware e2m1 conversion
+//   with the e8m0 scale.
+//
+// K order.  A step covers 256 K = 128 bytes of a weight row.  Load i (0, 1) of lane
+// (r = lane % 16, g = lane / 16) reads the 16 bytes at 32*g + 16*i of its row's step, so the
+// four lanes of a row fill the 128-byte line, and lane group g's NF4 pieces lie in 64-block g.
+// MFMA (i, q) takes dword q of load i: K = 64*g + 32*i + 8*q + [0, 8) inside the step; the
+// activation chunk with the same K is read from LDS for token r.  Activations and h are in
+// natural K order on this path (the table yields the two elements of a byte in order).
+#include "e4b_device.h"
+#include "e4b_internal.h"
+
+namespace e4b {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kStepK = 256;                        // K per pipeline step
+constexpr int kTok = kGemvTileRows;                 // routed rows per tile (MFMA N)
+constexpr int kActRowBytes = kStepK * 2;            // fp16 activations of one row per step
+constexpr int kActBufBytes = kTok * kActRowBytes;   // 8 KB per buffer
+constexpr int kLutBytes = 256 * 64 * 4;             // 64 KB: 256 pairs x 64 lane copies
+constexpr int kWgPerCu = 2;                         // LDS: 80 KB per workgroup with the table
+constexpr int kStages = 2;                          // register sets in the load ring
+
+static_assert(kTok == 16, "one MFMA pass of 16 routed rows per tile");
+
+// vector-memory operations per lane per step: 2 weight loads and 1 scale load per row block,
+// and 2 activation loads
+template <int RB>
+constexpr int ops_per_step() { return 3 * RB + 2; }
+
+// fp16 bit patterns of the NF4 codebook (QLoRA NormalFloat-4), code 0..15.
+__device__ __constant__ const uint16_t kNf4Half[16] = {
+    0xBC00, 0xB992, 0xB833, 0xB652, 0xB48D, 0xB1EA, 0xADD4, 0x0000,
+    0x2D18, 0x3126, 0x33E0, 0x3568, 0x370D, 0x3880, 0x39C9, 0x3C00};
+
+struct GemvArgs {
+  const _Float16* a;       // gate_up: x16 [T, K]; down: h [S, K] (natural K order)
+  const uint8_t* wq;       // packed weights [E, N, K/2]
+  const void* sc;          // NF4 float [E, N, K/64] | MXFP4 uint8 [E, N, K/32]
+  int64_t K;
+  int64_t N;               // weight rows per expert (2I for gate_up, H for down)
+  int64_t I;
+  int64_t T, S;            // tokens, routed rows (rows of x16 and of h)
+  int32_t k_top;
+  int32_t n_rblocks;       // weight-row blocks per expert
+};
+
+// Index arrays read with uniform addresses inside the persistent loop are separate
+// __restrict__ kernel arguments, so the compiler reads them with scalar loads, which do not
+// count against the vector-memory counter the pipeline waits on.
+struct Ptrs {
+  const int32_t* __restrict__ tiles;  // [n, 4]: expert, first sorted row, rows (<= 16), 0
+  const int32_t* __restrict__ slots;  // sorted slots [S]
+  void* __restrict__ out;             // gate_up: h fp16 [S, I]; down: y float [S, N] (sorted)
+};
+
+// Where a step's data come from; every field is uniform across the workgroup.
+struct StepInfo {
+  int32_t e, row0, rows, rb;
+  int32_t kstep;  // first K of the step
+  bool last;      // last step of its item
+};
+
+__device__ __forceinline__ StepInfo step_info(const GemvArgs& p, const Ptrs& q, int s, int nseg) {
+  StepInfo st;
+  const int it = s / nseg;
+  const int item = int(blockIdx.x) + it * int(gridDim.x);
+  const int seg = s - it * nseg;
+  const int mt = item / p.n_rblocks;
+  st.rb = item - mt * p.n_rblocks;
+  st.e = q.tiles[4 * mt];
+  st.row0 = q.tiles[4 * mt + 1];
+  st.rows = q.tiles[4 * mt + 2];
+  st.kstep = seg * kStepK;
+  st.last = seg == nseg - 1;
+  return st;
+}
+
+// Weight row of lane row r in row block b of this wave, for item row block rb (clamped;
+// results of clamped rows are never stored).  gate_up: a row block is 8 gate rows j..j+7 and
+// the 8 matching up rows.
+template <bool GU, int RB>
+__device__ __forceinline__ int32_t lane_row(const GemvArgs& p, int rb, int wave, int b, int r) {
+  if (GU) {
+    const int32_t I = int32_t(p.I);
+    int32_t j = rb * (kWaves * RB * 8) + (wave * RB + b) * 8 + (r & 7);
+    j = j < I ? j : I - 1;
+    return r < 8 ? j : I + j;
+  }
+  const int32_t N = int32_t(p.N);
+  const int32_t n = rb * (kWaves * RB * 16) + (wave * RB + b) * 16 + r;
+  return n < N ? n : N - 1;
+}
+
+// Activation chunk (8 fp16) L of row c sits at chunk position L ^ (c % 16) of the row, so the
+// 16 lanes of one B-operand read (16 rows, same L) hit 16 different 4-bank groups.
+__device__ __forceinline__ int xpos(int c, int L) { return L ^ (c & 15); }
+
+template <int RB>
+struct StepRegs {
+  u32x4 w[RB][2];   // packed weights
+  uint32_t sv[RB];  // NF4 absmax bits | MXFP4 two e8m0 bytes
+  u32x4 av[2];      // activations for LDS
+};
+
+// Buffer resource over `bytes` bytes at `base` (raw buffer, no stride).  Buffer loads take a
+// 32-bit per-lane offset plus a wave-uniform offset, so no 64-bit address arithmetic runs per
+// load, and a load entirely past `bytes` returns zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+
+// Issue every memory operation of one step, all unconditional, so the count per step is the
+// same for every wave.  Pieces past K read the next row (or zeros past the buffer); their
+// scale is forced to 0 where the data are used, and activation columns past K meet zero
+// weights.
+template <int FMT, bool GU, int RB>
+__device__ __forceinline__ void issue_step(const GemvArgs& p, const Ptrs& pt,
+                                           const StepInfo& st, int wave, int lane,
+                                           StepRegs<RB>& R) {
+  const int r = lane & 15, g = lane >> 4;
+  const uint32_t kb = uint32_t(p.K >> 1);               // packed bytes per row
+  const uint32_t nbs = uint32_t(FMT == 0 ? (p.K >> 6) * 4 : (p.K >> 5));  // scale bytes per row
+  const __amdgpu_buffer_rsrc_t wres =
+      rsrc(p.wq + int64_t(st.e) * p.N * kb, uint32_t(p.N) * kb);
+  const __amdgpu_buffer_rsrc_t sres =
+      rsrc(reinterpret_cast<const uint8_t*>(p.sc) + int64_t(st.e) * p.N * nbs, uint32_t(p.N) * nbs);
+  const int wso = st.kstep >> 1;                               // uniform byte offsets of the step
+  const int sso = FMT == 0 ? (st.kstep >> 6) * 4 : (st.kstep >> 5);
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const uint32_t row = uint32_t(lane_row<GU, RB>(p, st.rb, wave, b, r));
+    const uint32_t wo = row * kb + 32 * g;
+    R.w[b][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, wo, wso, 0));
+    R.w[b][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, wo + 16, wso, 0));
+    if (FMT == 0)
+      R.sv[b] = __builtin_amdgcn_raw_buffer_load_b32(sres, row * nbs + 4 * g, sso, 0);
+    else
+      R.sv[b] = __builtin_amdgcn_raw_buffer_load_b16(sres, row * nbs + 2 * g, sso, 0);
+  }
+  // activations: 16 rows x 512 B; wave w loads rows 4w..4w+3, lane l the 16 bytes of chunk
+  // position l % 32 of row 4w + 2h + l / 32.  Rows at or past the tile's row count repeat its
+  // last row (their MFMA columns are discarded).
+  const int64_t arows = GU ? p.T : p.S;
+  const __amdgpu_buffer_rsrc_t ares = rsrc(p.a, uint32_t(arows * p.K * 2));
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    // the two rows of this load are wave-uniform, so their sources come from scalar loads
+    const int c0 = 4 * wave + 2 * h, c1 = c0 + 1;
+    const int cs0 = c0 < st.rows ? c0 : st.rows - 1, cs1 = c1 < st.rows ? c1 : st.rows - 1;
+    const int32_t src0 = GU ? pt.slots[st.row0 + cs0] / p.k_top : st.row0 + cs0;
+    const int32_t src1 = GU ? pt.slots[st.row0 + cs1] / p.k_top : st.row0 + cs1;
+    const int c = (lane >> 5) ? c1 : c0;
+    const uint32_t src = uint32_t((lane >> 5) ? src1 : src0);
+    const uint32_t ao = src * uint32_t(p.K * 2) + 16 * uint32_t(xpos(c, lane & 31));
+    R.av[h] = __builtin_bit_cast(u32x4,
+                                 __builtin_amdgcn_raw_buffer_load_b128(ares, ao, st.kstep * 2, 0));
+  }
+}
+
+__device__ __forceinline__ void stage_acts(const u32x4 (&av)[2], int wave, int lane,
+                                           uint8_t* xbuf) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = 4 * wave + 2 * h + (lane >> 5);
+    *reinterpret_cast<u32x4*>(xbuf + c * kActRowBytes + 16 * (lane & 31)) = av[h];
+  }
+}
+
+// MFMAs of one step as one straight-line block.  Group n = ((i * 4 + q) * RB + b): dword q of
+// load i of row block b.  The table lookups (and, for the first row block, the activation
+// fragment) of group n + 2 are issued before group n is formed.
+template <int FMT, int RB, int NA>
+__device__ __forceinline__ void compute_step(int64_t krem, int lane, const StepRegs<RB>& R,
+                                             const uint8_t* xbuf, const uint8_t* lut,
+                                             f32x4 (&acc)[NA]) {
+  constexpr int NG = 8 * RB;
+  constexpr int D = 2;
+  const int r = lane & 15, g = lane >> 4;
+  const uint32_t lanebase = uint32_t(lane) << 2;
+  const uint8_t* xrow = xbuf + r * kActRowBytes;
+  // pieces past K contribute nothing (scale 0)
+  const bool valid = int64_t(64 * g) < krem;
+  f16x2 s16[RB];
+  float smx[RB][2];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    if (FMT == 0) {
+      const float sc = valid ? __uint_as_float(R.sv[b]) : 0.0f;
+      s16[b] = f16x2{(_Float16)sc, (_Float16)sc};
+    } else {
+      smx[b][0] = valid ? e8m0_to_f32(R.sv[b] & 0xFFu) : 0.0f;
+      smx[b][1] = valid ? e8m0_to_f32((R.sv[b] >> 8) & 0xFFu) : 0.0f;
+    }
+  }
+  uint32_t lk[NG][4];
+  f16x8 xb[8];
+  auto fetch = [&](int n) {
+    const int b = n % RB, iq = n / RB, i = iq >> 2, q = iq & 3;
+    if (b == 0) {
+      const int L = 8 * g + 4 * i + q;
+      xb[iq] = *reinterpret_cast<const f16x8*>(xrow + 16 * xpos(r, L));
+    }
+    if (FMT == 0) {
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) {
+        // byte bt of the dword -> table address (value << 8) | (lane << 2)
+        const uint32_t addr = perm(R.w[b][i][q], lanebase, 0x0C0C0400u + (uint32_t(bt) << 8));
+        lk[n][bt] = *reinterpret_cast<const uint32_t*>(lut + addr);
+      }
+    }
+  };
+#pragma unroll
+  for (int n = 0; n < D; ++n) fetch(n);
+#pragma unroll
+  for (int n = 0; n < NG; ++n) {
+    if (n + D < NG) fetch(n + D);
+    const int b = n % RB, iq = n / RB, i = iq >> 2, q = iq & 3;
+    uint32_t d[4];
+    if (FMT == 0) {
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) d[bt] = pk_mul_f16(lk[n][bt], s16[b]);
+    } else {
+      mxfp4_decode8(R.w[b][i][q], smx[b][i], d);
+    }
+    const f16x8 a = __builtin_bit_cast(f16x8, u32x4{d[0], d[1], d[2], d[3]});
+    const int ai = RB == 1 ? (n & 1) : b;
+    acc[ai] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, xb[iq], acc[ai], 0, 0, 0);
+    // keep the written order (lookahead loads before their use) through scheduling
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Results of one item.  acc of row block b: element i = D[row 4g + i of the block, token r].
+template <bool GU, int RB>
+__device__ __forceinline__ void store_block(const GemvArgs& p, const Ptrs& pt,
+                                            const StepInfo& st, int wave, int lane, int b,
+                                            const f32x4& acc) {
+  const int r = lane & 15, g = lane >> 4;
+  if (GU) {
+    // rows 0-7 are gate rows, 8-15 the matching up rows: lane groups 0/1 hold gate values,
+    // 2/3 the up values of the same (j, token)
+    float up[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) up[i] = __shfl_xor(acc[i], 32);
+    if (g < 2 && r < st.rows) {
+      _Float16* h = reinterpret_cast<_Float16*>(pt.out) + int64_t(st.row0 + r) * p.I;
+      const int32_t j0 = st.rb * (kWaves * RB * 8) + (wave * RB + b) * 8 + 4 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (j0 + i < int32_t(p.I)) h[j0 + i] = (_Float16)swiglu(acc[i], up[i]);
+    }
+  } else if (r < st.rows) {
+    float* y = reinterpret_cast<float*>(pt.out) + int64_t(st.row0 + r) * p.N;
+    const int32_t n0 = st.rb * (kWaves * RB * 16) + (wave * RB + b) * 16 + 4 * g;
+    if (n0 < int32_t(p.N)) *reinterpret_cast<f32x4*>(y + n0) = acc;  // N % 64 == 0
+  }
+}
+
+template <int FMT, bool GU, int RB>
+__global__ void __launch_bounds__(kThreads)
+    moe_gemv_kernel(GemvArgs p, const int32_t* __restrict__ tiles,
+                    const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ slots,
+                    void* __restrict__ out) {
+  const Ptrs pt{tiles, slots, out};
+  constexpr int kLut = FMT == 0 ? kLutBytes : 0;
+  constexpr int kOps = ops_per_step<RB>();
+  constexpr int NA = RB < 2 ? 2 : RB;  // accumulators (two alternating chains when RB == 1)
+  // one allocation: the table, then two activation buffers
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kLut + 2 * kActBufBytes];
+  uint8_t* const lut = smem;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_items = *n_tiles * p.n_rblocks;
+  if (int(blockIdx.x) >= n_items) return;  // uniform over the workgroup
+  const int nseg = int((p.K + kStepK - 1) / kStepK);
+  const int my_items = (n_items - int(blockIdx.x) + int(gridDim.x) - 1) / int(gridDim.x);
+  const int nsteps = my_items * nseg;
+  const int last = nsteps - 1;
+
+  if (FMT == 0) {
+    // table word (v, l) at byte v * 256 + l * 4 = fp16 pair (C[v >> 4], C[v & 15]): element
+    // 2b (high nibble) in the low half.  Thread t fills value t, all 64 lane copies.
+    const uint32_t pair = uint32_t(kNf4Half[tid >> 4]) | (uint32_t(kNf4Half[tid & 15]) << 16);
+    const u32x4 q4 = u32x4{pair, pair, pair, pair};
+    u32x4* dst = reinterpret_cast<u32x4*>(lut + tid * 256);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dst[i] = q4;
+  }
+
+  // Ring of kStages register sets: step s uses set s % kStages and LDS buffer s % 2; the loads
+  // of steps s + 1 .. s + kStages - 1 are in flight while step s is computed.  Past the last
+  // step the loads repeat it and are never used.  Step s's activations are written to LDS
+  // right before its barrier, and the barrier of step s + 1 also tells that every wave is done
+  // reading buffer s % 2, so one barrier per step suffices.  The loop has a single exit so the
+  // compiler's memory-counter bookkeeping stays exact (a mid-loop exit made it fall back to
+  // waiting for everything).
+  StepRegs<RB> R[kStages];
+  StepInfo ci[kStages];
+  f32x4 acc[NA];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int b = 0; b < kStages - 1; ++b) {
+    ci[b] = step_info(p, pt, b < last ? b : last, nseg);
+    issue_step<FMT, GU, RB>(p, pt, ci[b], wave, lane, R[b]);
+  }
+  constexpr int kPeriod = kStages % 2 ? 2 * kStages : kStages;  // (register set, LDS buffer)
+  for (int s = 0; s < nsteps; s += kPeriod) {
+#pragma unroll
+    for (int b2 = 0; b2 < kPeriod; ++b2) {
+      const int cur = b2 % kStages, nxt = (b2 + kStages - 1) % kStages;
+      const int sn = s + b2 + kStages - 1;
+      uint8_t* const xbuf = smem + kLut + (b2 & 1) * kActBufBytes;
+      ci[nxt] = step_info(p, pt, sn < last ? sn : last, nseg);
+      issue_step<FMT, GU, RB>(p, pt, ci[nxt], wave, lane, R[nxt]);
+      // step s + b2 has landed for this wave (later steps' loads may stay in flight) ...
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((kStages - 1) * kOps));
+      stage_acts(R[cur].av, wave, lane, xbuf);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((kStages - 1) * kOps));
+      // ... and for every wave, with its activations (and the table) in LDS
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      if (b2 == 0 || s + b2 < nsteps) {
+        compute_step<FMT, RB, NA>(p.K - ci[cur].kstep, lane, R[cur], xbuf, lut, acc);
+        if (ci[cur].last) {
+          if (RB == 1) {
+            store_block<GU, RB>(p, pt, ci[cur], wave, lane, 0, acc[0] + acc[1]);
+          } else {
+#pragma unroll
+            for (int b = 0; b < RB; ++b)
+              store_block<GU, RB>(p, pt, ci[cur], wave, lane, b, acc[b]);
+          }
+#pragma unroll
+          for (int a = 0; a < NA; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+  }
+}
+
+#define E4B_GEMV_INST(FMT, GU, RB)                                                  \
+  template __global__ void moe_gemv_kernel<FMT, GU, RB>(                             \
+      GemvArgs, const int32_t*, const int32_t*, const int32_t*, void*);
+#define E4B_GEMV_INST_RB(FMT, GU) \
+  E4B_GEMV_INST(FMT, GU, 1) E4B_GEMV_INST(FMT, GU, 2) E4B_GEMV_INST(FMT, GU, 4)
+E4B_GEMV_INST_RB(0, true)
+E4B_GEMV_INST_RB(0, false)
+E4B_GEMV_INST_RB(1, true)
+E4B_GEMV_INST_RB(1, false)
+
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <int FMT, bool GU, int RB>
+hipError_t launch_rb(const GemvArgs& g, const MoeLaunch& L, void* out, int64_t n_out,
+                     int64_t wgs, hipStream_t stream) {
+  constexpr int64_t kPerItem = kWaves * RB * (GU ? 8 : 16);  // output rows (gate_up: j) per item
+  GemvArgs a = g;
+  a.n_rblocks = int((n_out + kPerItem - 1) / kPerItem);
+  const int64_t max_items = L.max_mtiles * a.n_rblocks;
+  int64_t grid = wgs < max_items ? wgs : max_items;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL((moe_gemv_kernel<FMT, GU, RB>), dim3(unsigned(grid)), dim3(kThreads), 0,
+                     stream, a, L.tiles, L.n_mtiles, L.slots, out);
+  return hipGetLastError();
+}
+
+// Row blocks per wave: the largest of 4, 2, 1 that still gives every resident workgroup an
+// item (the tile count is a device value; its host-side upper bound is used).
+template <int FMT, bool GU>
+hipError_t launch_stage(const GemvArgs& g, const MoeLaunch& L, void* out, int64_t n_out,
+                        hipStream_t stream) {
+  const int64_t wgs = int64_t(kWgPerCu) * cu_count();
+  const int64_t per_block = GU ? 8 : 16;
+  auto items = [&](int64_t rb) {
+    const int64_t per_item = kWaves * rb * per_block;
+    return L.max_mtiles * ((n_out + per_item - 1) / per_item);
+  };
+  if (items(4) >= wgs) return launch_rb<FMT, GU, 4>(g, L, out, n_out, wgs, stream);
+  if (items(2) >= wgs) return launch_rb<FMT, GU, 2>(g, L, out, n_out, wgs, stream);
+  return launch_rb<FMT, GU, 1>(g, L, out, n_out, wgs, stream);
+}
+
+}  // namespace
+
+template <int FMT>
+static hipError_t launch_gemv_fmt(const MoeLaunch& L, hipStream_t stream, int stage) {
+  GemvArgs g{};
+  g.k_top = L.k;
+  g.I = L.I;
+  g.T = L.T;
+  g.S = L.T * L.k;
+  if (stage == 0) {
+    g.a = L.x16;
+    g.wq = L.w_gu;
+    g.sc = L.s_gu;
+    g.K = L.H;
+    g.N = 2 * L.I;
+    return launch_stage<FMT, true>(g, L, L.h, L.I, stream);
+  }
+  g.a = L.h;
+  g.wq = L.w_dn;
+  g.sc = L.s_dn;
+  g.K = L.I;
+  g.N = L.H;
+  return launch_stage<FMT, false>(g, L, L.y, L.H, stream);
+}
+
+hipError_t launch_gemv(const MoeLaunch& L, hipStream_t stream, int stage) {
+  return L.fmt == 0 ? launch_gemv_fmt<0>(L, stream, stage) : launch_gemv_fmt<1>(L, stream, stage);
+}
+
+}  // namespace e4b

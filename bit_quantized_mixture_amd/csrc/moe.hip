@@ -10,8 +10,9 @@
 //   convert_x     x bf16 [T,H] -> fp16 (exact in fp16 range), k-slot order of the format
 //   build_tiles   per expert, ceil(rows/BM) row tiles of the expert-major slot order
 //   gemm<GU>      h[p, j] = silu(x_t . Wg[e,j]) * (x_t . Wu[e,j]) for the rows p of a tile
-//   gemm<DN>      y[s, n] = topk_w[s] * (h[p] . Wd[e,n])   (s = slot of sorted row p)
-//   combine       out[t] = sum_j y[t*k+j]  (fixed order)  -> fp32 and bf16 (RNE)
+//   gemm<DN>      y[p, n] = h[p] . Wd[e,n]   (sorted row p)
+//   combine       out[t] = sum_j topk_w[s] * y[inv[s]], s = t*k+j  (fixed order) -> fp32, bf16
+//                 (RNE); inv (slot -> sorted row) is written by convert_x
 //
 // Tile structure of gemm: a workgroup owns BM rows of one expert and WAVES*64 weight rows
 // (GU: 32 gate + 32 matching up rows per wave, so SwiGLU is formed in registers).  Each
@@ -42,7 +43,6 @@ struct GemmArgs {
   const int32_t* tiles;    // [max_mtiles, 4]: expert, first sorted row, rows, 0
   const int32_t* n_mtiles;
   const int32_t* slots;    // sorted slots [S]
-  const float* topk_w;     // [S]
   void* out;               // GU: h fp16 [S, I]; DN: y float [S, N]
   int64_t K;
   int64_t N;               // weight rows per expert (2I for GU, H for DN)
@@ -51,17 +51,6 @@ struct GemmArgs {
   int32_t n_ntiles;
 };
 
-// Position of h column j inside its row, in the k-slot order the down GEMM reads.
-template <int FMT>
-__device__ __forceinline__ int64_t act_pos(int64_t j) {
-  if (FMT == 0) return (j & ~int64_t(7)) | nf4_elem_slot(int(j & 7));
-  return j;
-}
-
-// s_waitcnt immediate: vmcnt = vm (0..63), expcnt = 7 (no wait), lgkmcnt = 0.
-__host__ __device__ constexpr int waitcnt_vm_lgkm0(int vm) {
-  return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4);
-}
 
 template <int FMT, bool GU, int BM, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
@@ -340,11 +329,9 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
       for (int r = 0; r < 16; ++r) {
         const int row = 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3);
         if (row < rows) {
-          const int32_t slot = p.slots[row0 + row];
-          const float wgt = p.topk_w[slot];
 #pragma unroll
           for (int f = 0; f < 2; ++f)
-            if (nvalid[f]) y[int64_t(slot) * p.N + nrow[f]] = wgt * acc[rb][f][r];
+            if (nvalid[f]) y[int64_t(row0 + row) * p.N + nrow[f]] = acc[rb][f][r];
         }
       }
     }
@@ -363,13 +350,19 @@ E4B_GEMM_INST_ALL(0)
 E4B_GEMM_INST_ALL(1)
 
 // x bf16 -> fp16 (exact for |x| in fp16's normal range), stored in the k-slot order of the
-// weight format inside each aligned group of 8.
+// weight format inside each aligned group of 8.  Also inverts the routing permutation:
+// inv[slots[p]] = p for the S sorted rows p.
 template <int FMT>
 __global__ void __launch_bounds__(256) convert_x_kernel(const uint16_t* __restrict__ x,
                                                         _Float16* __restrict__ x16,
-                                                        int64_t n_chunks) {
+                                                        int64_t n_chunks,
+                                                        const int32_t* __restrict__ slots,
+                                                        int64_t S, int32_t* __restrict__ inv) {
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  for (int64_t q = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; q < n_chunks; q += stride) {
+  const int64_t n = n_chunks > S ? n_chunks : S;
+  for (int64_t q = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; q < n; q += stride) {
+    if (q < S) inv[slots[q]] = int32_t(q);
+    if (q >= n_chunks) continue;
     const u32x4 raw = *reinterpret_cast<const u32x4*>(x + 8 * q);
     _Float16 v[8];
 #pragma unroll
@@ -426,8 +419,11 @@ __global__ void __launch_bounds__(256) build_tiles_kernel(const int32_t* __restr
   if (tid == 0) *n_mtiles = run;
 }
 
-// out[t, :] = sum_{j<k} y[t*k + j, :], fixed order; fp32 and bf16 (RNE) outputs.
-__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ y, int64_t T,
+// out[t, :] = sum_{j<k} topk_w[s] * y[inv[s], :] with s = t*k + j, fixed order; fp32 and
+// bf16 (RNE).
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ y,
+                                                      const float* __restrict__ topk_w,
+                                                      const int32_t* __restrict__ inv, int64_t T,
                                                       int64_t H, int k,
                                                       uint16_t* __restrict__ out,
                                                       float* __restrict__ out_f32) {
@@ -437,7 +433,9 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     const int64_t t = q / (H / 4);
     const int64_t c = (q - t * (H / 4)) * 4;
     f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) s += *reinterpret_cast<const f32x4*>(y + (t * k + j) * H + c);
+    for (int j = 0; j < k; ++j)
+      s += topk_w[t * k + j] *
+           *reinterpret_cast<const f32x4*>(y + int64_t(inv[t * k + j]) * H + c);
     if (out_f32) *reinterpret_cast<f32x4*>(out_f32 + t * H + c) = s;
     u32x2 o;
     o[0] = uint32_t(f32_to_bf16_rne(s[0])) | (uint32_t(f32_to_bf16_rne(s[1])) << 16);
@@ -463,7 +461,6 @@ static hipError_t launch_gemms(const MoeLaunch& L, hipStream_t stream) {
   g.tiles = L.tiles;
   g.n_mtiles = L.n_mtiles;
   g.slots = L.slots;
-  g.topk_w = L.topk_w;
   g.k_top = L.k;
   g.I = L.I;
   // gate_up + SwiGLU
@@ -493,14 +490,25 @@ static hipError_t launch_gemms(const MoeLaunch& L, hipStream_t stream) {
 template <int FMT>
 static hipError_t launch_fmt(const MoeLaunch& L, hipStream_t stream) {
   record(L, 0, stream);
-  hipLaunchKernelGGL(convert_x_kernel<FMT>, dim3(grid_1d(L.T * L.H / 8)), dim3(256), 0, stream,
-                     L.x, L.x16, L.T * L.H / 8);
+  // the streaming path takes activations in natural order for both formats
+  const int64_t S = L.T * L.k, nchunks = L.T * L.H / 8;
+  const unsigned gx = grid_1d(nchunks > S ? nchunks : S);
+  if (FMT == 0 && !L.cfg.gemv)
+    hipLaunchKernelGGL(convert_x_kernel<0>, dim3(gx), dim3(256), 0, stream, L.x, L.x16, nchunks,
+                       L.slots, S, L.inv);
+  else
+    hipLaunchKernelGGL(convert_x_kernel<1>, dim3(gx), dim3(256), 0, stream, L.x, L.x16, nchunks,
+                       L.slots, S, L.inv);
   record(L, 1, stream);
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, stream, L.offsets, int(L.E),
                      L.cfg.bm, L.tiles, L.n_mtiles);
   record(L, 2, stream);
   hipError_t err;
-  if (L.cfg.bm == 256)
+  if (L.cfg.gemv) {
+    err = launch_gemv(L, stream, 0);
+    record(L, 3, stream);
+    if (err == hipSuccess) err = launch_gemv(L, stream, 1);
+  } else if (L.cfg.bm == 256)
     err = launch_gemms<FMT, 256, 4>(L, stream);
   else if (L.cfg.bm == 128)
     err = launch_gemms<FMT, 128, 4>(L, stream);
@@ -508,8 +516,8 @@ static hipError_t launch_fmt(const MoeLaunch& L, hipStream_t stream) {
     err = launch_gemms<FMT, 32, 1>(L, stream);
   if (err != hipSuccess) return err;
   record(L, 4, stream);
-  hipLaunchKernelGGL(combine_kernel, dim3(grid_1d(L.T * L.H / 4)), dim3(256), 0, stream, L.y, L.T,
-                     L.H, L.k, L.out, L.out_f32);
+  hipLaunchKernelGGL(combine_kernel, dim3(grid_1d(L.T * L.H / 4)), dim3(256), 0, stream, L.y,
+                     L.topk_w, L.inv, L.T, L.H, L.k, L.out, L.out_f32);
   record(L, 5, stream);
   return hipGetLastError();
 }

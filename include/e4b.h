@@ -63,11 +63,12 @@ typedef enum e4b_fmt { E4B_FMT_NF4 = 0, E4B_FMT_MXFP4 = 1 } e4b_fmt;
  * when the mean routed rows per expert T*k/E is below 16, the MFMA tile path otherwise.
  * The choice depends only on host-known sizes; no device value is read back. */
 #define E4B_PATH_AUTO 0x0
-#define E4B_PATH_GEMM 0x1 /* MFMA grouped GEMM, 256-row tiles */
-#define E4B_PATH_GEMV 0x2 /* small-M streaming path, 32-row tiles */
+#define E4B_PATH_GEMM 0x1 /* MFMA grouped GEMM, 128- or 256-row tiles */
+#define E4B_PATH_GEMV 0x2 /* small-M streaming path: tiles of <= 64 rows, weights streamed once */
 #define E4B_PATH_MASK 0x3
 /* e4b_moe_args.flags bits 2-3: row-tile override for the MFMA path (0 = chosen from the
- * sizes): 32 rows (1 wave), 128 rows (4 waves), 256 rows (4 waves). */
+ * sizes): 32 rows (1 wave), 128 rows (4 waves), 256 rows (4 waves).  An override selects
+ * the MFMA path under E4B_PATH_AUTO; with E4B_PATH_GEMV it is E4B_ERR_ARG. */
 #define E4B_TILE_AUTO 0x0
 #define E4B_TILE_32 0x4
 #define E4B_TILE_128 0x8

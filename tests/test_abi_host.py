@@ -104,6 +104,7 @@ def test_forward_rejects_bad_arguments(e4b):
     assert f(flags=3) == ERR_ARG
     assert f(flags=0x10) == ERR_ARG
     assert f(flags=7) == ERR_ARG
+    assert f(flags=0x6) == ERR_ARG                   # tile override with the streaming path
     assert f(H=96) == ERR_SHAPE
     assert f(I=100) == ERR_SHAPE
     assert f(x=None) == ERR_ARG

@@ -47,6 +47,20 @@ def test_small_layers(e4b, fmt, path, E, H, I, T, k):
 
 
 @pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
+@pytest.mark.parametrize("E,H,I,T,k", [
+    (4, 2880, 192, 5, 2),      # gate_up K = 2880: three K steps of the streaming kernel, last partial
+    (3, 128, 2112, 7, 1),      # down K = 2112: last step of 64
+    (32, 512, 1024, 200, 4),   # more work items than resident workgroups: several items each
+])
+def test_streaming_path_long_k_and_many_items(e4b, fmt, E, H, I, T, k):
+    layer = random_layer(e4b, fmt, E, H, I, T, k, seed=H + I + T)
+    for path in (PATHS["gemv"], PATHS["gemm"]):
+        out, out32 = layer.forward(path)
+        assert_rows_within_tolerance(out32, layer.oracle_out(), f"{fmt}/{path}/{E},{H},{I},{T},{k}")
+        assert_out_is_rne_of_f32(out, out32)
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
 def test_skewed_routing_with_empty_experts_and_a_hot_expert(e4b, fmt):
     E = 12
     bias = np.full(E, -30.0)
@@ -83,3 +97,48 @@ def test_zero_input_gives_zero_output(e4b, tiny):
                                      tiny.k, out_f32=True)
     torch.cuda.synchronize()
     assert torch.count_nonzero(out32).item() == 0
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_graph_replay_matches_eager(e4b, path):
+    """route + forward captured in a HIP graph: every replay (with eager work and
+    synchronisations in between) reproduces the eager result bit for bit."""
+    layer = random_layer(e4b, "nf4", 16, 256, 256, 24, 4, seed=11)
+    T, k, E = layer.T, layer.k, layer.E
+    dev = "cuda:0"
+    route_out = (torch.empty((T, k), dtype=torch.int32, device=dev),
+                 torch.empty((T, k), dtype=torch.float32, device=dev),
+                 torch.empty((E + 1,), dtype=torch.int32, device=dev),
+                 torch.empty((T * k,), dtype=torch.int32, device=dev))
+    rws = torch.empty(max(256, e4b.e4b_route_workspace_bytes(T, E, k)), dtype=torch.uint8, device=dev)
+    fws = torch.empty(max(256, e4b.e4b_moe_workspace_bytes("nf4", E, layer.H, layer.I, T, k, path)),
+                      dtype=torch.uint8, device=dev)
+    out = torch.empty((T, layer.H), dtype=torch.bfloat16, device=dev)
+    out32 = torch.empty((T, layer.H), dtype=torch.float32, device=dev)
+
+    def step():
+        ids, w, off, slots = e4b.e4b_route_permute(layer.logits_dev, k, ws=rws, out=route_out)
+        e4b.e4b_moe_forward("nf4", layer.x, layer.gp, layer.gs, layer.dp, layer.ds, w, off, slots, k,
+                            out=out, out_f32=out32, ws=fws, path=path)
+
+    step()
+    torch.cuda.synchronize()
+    ref = out32.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(4):
+        out32.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out32, ref)
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out32, ref)
