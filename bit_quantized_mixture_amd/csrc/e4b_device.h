@@ -124,6 +124,23 @@ __host__ __device__ constexpr int waitcnt_vm_lgkm0(int vm) {
   return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4);
 }
 
+// Raw buffer resource over `bytes` bytes at `base` (no stride): buffer loads take a 32-bit
+// per-lane byte offset, and a load entirely past `bytes` returns zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+
+// Direct buffer -> LDS copy of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane i's bytes
+// (from byte offset voff of the buffer) land at lds_wave_base + 16 * i.  Unlike the FLAT form
+// (global_load_lds), a copy of this kind in flight leaves the compiler's LDS-read waits exact.
+__device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t res, uint32_t voff,
+                                              void* lds_wave_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) void lds_void;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(res, (lds_void*)lds_wave_base, 16, int(voff), 0, 0, 0);
+#endif
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
 // SiLU(g) * u in fp32 with the hardware exp and reciprocal (the result is stored as fp16).

@@ -47,6 +47,7 @@ struct GemmArgs {
   int64_t K;
   int64_t N;               // weight rows per expert (2I for GU, H for DN)
   int64_t I;
+  int64_t T;               // tokens (rows of x16; h has T * k_top rows)
   int32_t k_top;
   int32_t n_ntiles;
 };
@@ -151,6 +152,8 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
   uint32_t sraw[2][2][2];
   int gld[2];          // group index loaded into each slot (for validity)
 
+  const __amdgpu_buffer_rsrc_t ares =
+      buffer_rsrc(p.a, uint32_t((GU ? int64_t(p.T) : int64_t(p.T) * p.k_top) * p.K * 2));
   auto stage_a = [&](int kb, int buf) {
     const uint32_t kg = uint32_t(256 * (kb >> 2) + 32 * (kb & 3));
 #pragma unroll
@@ -158,7 +161,7 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
       const int par = ((wave * ROWS_W) / 8 + j) & 1;
       uint32_t ko = kg + apart2[par];
       ko = ko < kmax_a ? ko : kmax_a;
-      lds_dma16(p.a + arow_off[j] + ko, &lds[buf][wave * ROWS_W + 8 * j][0]);
+      lds_dma16_buf(ares, 2 * (arow_off[j] + ko), &lds[buf][wave * ROWS_W + 8 * j][0]);
     }
   };
   auto load_group = [&](int G, int slot) {
@@ -463,6 +466,7 @@ static hipError_t launch_gemms(const MoeLaunch& L, hipStream_t stream) {
   g.slots = L.slots;
   g.k_top = L.k;
   g.I = L.I;
+  g.T = L.T;
   // gate_up + SwiGLU
   g.a = L.x16;
   g.wq = L.w_gu;
