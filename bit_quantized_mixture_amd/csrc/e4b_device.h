@@ -65,6 +65,40 @@ __device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel)
   return __builtin_amdgcn_perm(s0, s1, sel);
 }
 
+// (3) LDS decode table: for each packed byte value v, the fp16 pair (C[v >> 4], C[v & 15])
+//     (element 2b, the high nibble, in the low half), with one private copy per lane: the
+//     word for (v, lane l) sits at byte v * 256 + l * 4, so lane l always reads LDS bank l
+//     and the 64 lookups of a wave never conflict.  64 KB.
+constexpr int kNf4LutBytes = 256 * 64 * 4;
+
+// fp16 bit patterns of the codebook (form (1) above, as 16-bit values), code 0..15.
+__device__ __constant__ const uint16_t kNf4Half[16] = {
+    0xBC00, 0xB992, 0xB833, 0xB652, 0xB48D, 0xB1EA, 0xADD4, 0x0000,
+    0x2D18, 0x3126, 0x33E0, 0x3568, 0x370D, 0x3880, 0x39C9, 0x3C00};
+
+// Fill the table at `lut` (kNf4LutBytes of LDS) with `nthreads` threads of the workgroup
+// (nthreads divides 256 * 16); visible to other waves after the next barrier.
+__device__ __forceinline__ void nf4_lut_fill(uint8_t* lut, int tid, int nthreads) {
+  typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+  for (int c = tid; c < 256 * 16; c += nthreads) {  // 16-byte chunks: value c / 16
+    const int v = c >> 4;
+    const uint32_t pair = uint32_t(kNf4Half[v >> 4]) | (uint32_t(kNf4Half[v & 15]) << 16);
+    *reinterpret_cast<v4*>(lut + 16 * c) = v4{pair, pair, pair, pair};
+  }
+}
+
+// Decode one packed NF4 dword (8 codes) through the LDS table to 8 fp16 codebook values in
+// element order: out[b] = (element 2b, element 2b+1).  lanebase = lane * 4.  One v_perm
+// builds each lookup address (byte value << 8 | lanebase).
+__device__ __forceinline__ void nf4_lut_decode8(const uint8_t* lut, uint32_t lanebase, uint32_t w,
+                                                uint32_t out[4]) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t addr = perm(w, lanebase, 0x0C0C0400u + (uint32_t(b) << 8));
+    out[b] = *reinterpret_cast<const uint32_t*>(lut + addr);
+  }
+}
+
 // Bitfield select: bits of a where mask is 1, bits of b elsewhere (v_bfi_b32).
 __device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) {
   return (mask & a) | (~mask & b);

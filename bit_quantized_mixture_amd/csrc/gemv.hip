@@ -42,7 +42,7 @@ constexpr int kStepK = 256;                        // K per pipeline step
 constexpr int kTok = kGemvTileRows;                 // routed rows per tile (MFMA N)
 constexpr int kActRowBytes = kStepK * 2;            // fp16 activations of one row per step
 constexpr int kActBufBytes = kTok * kActRowBytes;   // 8 KB per buffer
-constexpr int kLutBytes = 256 * 64 * 4;             // 64 KB: 256 pairs x 64 lane copies
+constexpr int kLutBytes = kNf4LutBytes;            // 64 KB: 256 pairs x 64 lane copies
 constexpr int kWgPerCu = 2;                         // LDS: 80 KB per workgroup with the table
 constexpr int kStages = 2;                          // register sets in the load ring
 
@@ -52,11 +52,6 @@ static_assert(kTok == 16, "one MFMA pass of 16 routed rows per tile");
 // and 2 activation loads
 template <int RB>
 constexpr int ops_per_step() { return 3 * RB + 2; }
-
-// fp16 bit patterns of the NF4 codebook (QLoRA NormalFloat-4), code 0..15.
-__device__ __constant__ const uint16_t kNf4Half[16] = {
-    0xBC00, 0xB992, 0xB833, 0xB652, 0xB48D, 0xB1EA, 0xADD4, 0x0000,
-    0x2D18, 0x3126, 0x33E0, 0x3568, 0x370D, 0x3880, 0x39C9, 0x3C00};
 
 struct GemvArgs {
   const _Float16* a;       // gate_up: x16 [T, K]; down: h [S, K] (natural K order)
@@ -304,15 +299,7 @@ __global__ void __launch_bounds__(kThreads)
   const int nsteps = my_items * nseg;
   const int last = nsteps - 1;
 
-  if (FMT == 0) {
-    // table word (v, l) at byte v * 256 + l * 4 = fp16 pair (C[v >> 4], C[v & 15]): element
-    // 2b (high nibble) in the low half.  Thread t fills value t, all 64 lane copies.
-    const uint32_t pair = uint32_t(kNf4Half[tid >> 4]) | (uint32_t(kNf4Half[tid & 15]) << 16);
-    const u32x4 q4 = u32x4{pair, pair, pair, pair};
-    u32x4* dst = reinterpret_cast<u32x4*>(lut + tid * 256);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dst[i] = q4;
-  }
+  if (FMT == 0) nf4_lut_fill(lut, tid, kThreads);
 
   // Ring of kStages register sets: step s uses set s % kStages and LDS buffer s % 2; the loads
   // of steps s + 1 .. s + kStages - 1 are in flight while step s is computed.  Past the last
