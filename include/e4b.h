@@ -64,7 +64,8 @@ typedef enum e4b_fmt { E4B_FMT_NF4 = 0, E4B_FMT_MXFP4 = 1 } e4b_fmt;
  * The choice depends only on host-known sizes; no device value is read back. */
 #define E4B_PATH_AUTO 0x0
 #define E4B_PATH_GEMM 0x1 /* MFMA grouped GEMM, 128- or 256-row tiles */
-#define E4B_PATH_GEMV 0x2 /* small-M streaming path: tiles of <= 64 rows, weights streamed once */
+#define E4B_PATH_GEMV 0x2 /* small-M streaming path: 16-row tiles, each expert's weights streamed
+                           * once per 16 routed rows */
 #define E4B_PATH_MASK 0x3
 /* e4b_moe_args.flags bits 2-3: row-tile override for the MFMA path (0 = chosen from the
  * sizes): 32 rows (1 wave), 128 rows (4 waves), 256 rows (4 waves).  An override selects

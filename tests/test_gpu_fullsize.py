@@ -1,0 +1,75 @@
+"""Full-size forward parity on sampled tokens.
+
+Each full-size workload runs through the GPU path exactly as bench.py launches it (GPU
+packing, e4b_route_permute, e4b_moe_forward with the automatic path choice) and the sampled
+tokens' outputs are compared with float64 oracle outputs stored by
+tests/golden/make_expected.py (which calls only the oracle).  Properties checked on every
+row: the bf16 output is the round-to-nearest-even of the fp32 output.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import assert_out_is_rne_of_f32, assert_rows_within_tolerance, host
+from moe_inputs import WORKLOADS, make_expert_weight, make_logits, make_x
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+DEV = "cuda:0"
+CASES = [
+    ("mixtral_nf4_prefill", "mixtral_nf4_prefill", None),
+    ("finegrained_nf4_decode_T1", "finegrained_nf4_decode", 1),
+    ("finegrained_nf4_decode_T4", "finegrained_nf4_decode", 4),
+    ("finegrained_nf4_decode_T16", "finegrained_nf4_decode", 16),
+    ("finegrained_nf4_decode_T64", "finegrained_nf4_decode", 64),
+    ("mxfp4_moe", "mxfp4_moe", None),
+    ("skewed_nf4_prefill", "skewed_nf4_prefill", None),
+]
+
+_packed_cache = {}
+
+
+def packed_layer(e4b, wl):
+    """GPU-packed gate_up / down stacks of a workload (weights generated expert by expert)."""
+    if wl.name in _packed_cache:
+        return _packed_cache[wl.name]
+    _packed_cache.clear()
+    torch.cuda.empty_cache()
+    out = {}
+    for which, (N, K) in (("gate_up", (2 * wl.I, wl.H)), ("down", (wl.H, wl.I))):
+        w = torch.empty((wl.E, N, K), dtype=torch.bfloat16, device=DEV)
+        for e in range(wl.E):
+            w[e].copy_(torch.from_numpy(make_expert_weight(wl, which, e).view(np.int16)).view(torch.bfloat16))
+        out[which] = e4b.e4b_pack_nf4(w) if wl.fmt == "nf4" else e4b.e4b_pack_mxfp4(w)
+        del w
+    torch.cuda.synchronize()
+    _packed_cache[wl.name] = out
+    return out
+
+
+@pytest.mark.parametrize("case,name,T", CASES, ids=[c[0] for c in CASES])
+def test_full_size_sampled_tokens(e4b, case, name, T):
+    path = os.path.join(GOLDEN, f"expected_{case}.npz")
+    if not os.path.exists(path):
+        pytest.fail(f"{path} missing: run tests/golden/make_expected.py")
+    exp = np.load(path)
+    wl = WORKLOADS[name] if T is None else WORKLOADS[name].with_T(T)
+    packed = packed_layer(e4b, wl)
+    x = torch.from_numpy(make_x(wl).view(np.int16)).to(DEV).view(torch.bfloat16)
+    logits = torch.from_numpy(make_logits(wl)).to(DEV)
+    ids, w, off, slots = e4b.e4b_route_permute(logits, wl.k)
+    gp, gs = packed["gate_up"]
+    dp, ds = packed["down"]
+    out, out32 = e4b.e4b_moe_forward(wl.fmt, x, gp, gs, dp, ds, w, off, slots, wl.k, out_f32=True)
+    torch.cuda.synchronize()
+    toks = exp["tokens"]
+    # routing of the sampled tokens: ids bit-exact, weights to fp32 precision
+    np.testing.assert_array_equal(host(ids)[toks], exp["ids"])
+    np.testing.assert_allclose(host(w)[toks], exp["w"], rtol=2e-6, atol=1e-7)
+    o32 = host(out32)
+    assert np.all(np.isfinite(o32))
+    assert_rows_within_tolerance(o32[toks], exp["out"], case)
+    assert_out_is_rne_of_f32(host(out), o32)
