@@ -10,7 +10,7 @@ moe_inputs.py.  Prints ONE JSON line on stdout; progress goes to stderr.
 The headline workload is the Mixtral-shaped NF4 prefill layer (E=8, H=4096, I=14336, top-2,
 T=4096).  The same line carries, under "secondary", the skewed 64-expert prefill layer, the
 MXFP4 layer and the 128-expert decode layer at T = 64, 16, 4, 1 (warm, and cold with the
-256 MB Infinity Cache flushed before every step; eager launches with per-stage HIP events,
+256 MB Infinity Cache flushed by reading 1 GiB before every step; eager launches with per-stage HIP events,
 and the same step replayed from a HIP graph), and a float64 CPU-oracle baseline timed on a
 bounded sample of the headline workload.
 """
@@ -112,8 +112,10 @@ class Batch:
 def measure(torch, b: Batch, steps: int, warmup: int, flush_bytes: int = 0):
     """Time `steps` route+forward steps.  Per-stage kernel times come from HIP events the
     library records on the stream it launches on.  With flush_bytes > 0, a buffer of that
-    size is overwritten before each step (outside the events) so weights come from HBM."""
-    flush = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda:0") if flush_bytes else None
+    size is read (summed) before each step, outside the events, so the weights come from HBM.
+    The flush reads rather than writes: a written buffer leaves dirty lines in the caches,
+    and writing them back during the step would be charged to the kernels."""
+    flush = torch.zeros(flush_bytes // 4, dtype=torch.int32, device="cuda:0") if flush_bytes else None
     for _ in range(warmup):
         b.step()
     torch.cuda.synchronize()
@@ -129,7 +131,7 @@ def measure(torch, b: Batch, steps: int, warmup: int, flush_bytes: int = 0):
     t_begin.record()
     for i in range(steps):
         if flush is not None:
-            flush.fill_(i & 0xFF)
+            flush.sum()
         step_ev[i][0].record()
         b.step(ev[i])
         step_ev[i][1].record()

@@ -3,8 +3,9 @@
 // streaming the packed weights once (grouped-nf4-gemm 0.25.0 project description: the decode
 // GEMV beside the grouped GEMM), so this kernel is built around HBM throughput:
 //
-// * Persistent workgroups of 4 waves, two per CU.  A work item is (tile of <= 16 routed rows
-//   of one expert, block of 64 * RB weight rows); each wave owns RB row blocks of 16 rows.  A
+// * Persistent workgroups of 8 waves, two per CU (16 waves per CU, four per SIMD, so one
+//   wave's compute overlaps the others' loads).  A work item is (tile of <= 16 routed rows of
+//   one expert, block of 128 * RB weight rows); each wave owns RB row blocks of 16 rows.  A
 //   workgroup walks its items and, inside each item, K in steps of 256, as one flat sequence.
 // * 16x16x32 f16 MFMA with the weights as the A operand and the routed activations as B (16
 //   columns): D[row, token] += sum_k W[row, k] * X[token, k].  One activation fragment read
@@ -36,7 +37,7 @@ namespace e4b {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kStepK = 256;                        // K per pipeline step
 constexpr int kTok = kGemvTileRows;                 // routed rows per tile (MFMA N)
@@ -45,13 +46,16 @@ constexpr int kActBufBytes = kTok * kActRowBytes;   // 8 KB per buffer
 constexpr int kLutBytes = kNf4LutBytes;            // 64 KB: 256 pairs x 64 lane copies
 constexpr int kWgPerCu = 2;                         // LDS: 80 KB per workgroup with the table
 constexpr int kStages = 2;                          // register sets in the load ring
+constexpr int kActLoads = kTok / (2 * kWaves);      // activation loads (two rows each) per wave
+constexpr int kMaxRB = kWaves >= 8 ? 2 : 4;         // row blocks per wave (VGPR budget)
 
 static_assert(kTok == 16, "one MFMA pass of 16 routed rows per tile");
+static_assert(kActLoads >= 1 && kTok == 2 * kWaves * kActLoads, "activation rows per wave");
 
 // vector-memory operations per lane per step: 2 weight loads and 1 scale load per row block,
-// and 2 activation loads
+// and the activation loads
 template <int RB>
-constexpr int ops_per_step() { return 3 * RB + 2; }
+constexpr int ops_per_step() { return 3 * RB + kActLoads; }
 
 struct GemvArgs {
   const _Float16* a;       // gate_up: x16 [T, K]; down: h [S, K] (natural K order)
@@ -120,7 +124,7 @@ template <int RB>
 struct StepRegs {
   u32x4 w[RB][2];   // packed weights
   uint32_t sv[RB];  // NF4 absmax bits | MXFP4 two e8m0 bytes
-  u32x4 av[2];      // activations for LDS
+  u32x4 av[kActLoads];  // activations for LDS
 };
 
 // Buffer resource over `bytes` bytes at `base` (raw buffer, no stride).  Buffer loads take a
@@ -158,15 +162,15 @@ __device__ __forceinline__ void issue_step(const GemvArgs& p, const Ptrs& pt,
     else
       R.sv[b] = __builtin_amdgcn_raw_buffer_load_b16(sres, row * nbs + 2 * g, sso, 0);
   }
-  // activations: 16 rows x 512 B; wave w loads rows 4w..4w+3, lane l the 16 bytes of chunk
-  // position l % 32 of row 4w + 2h + l / 32.  Rows at or past the tile's row count repeat its
-  // last row (their MFMA columns are discarded).
+  // activations: 16 rows x 512 B; wave w loads rows 2Aw .. 2Aw + 2A - 1 (A = kActLoads), lane
+  // l the 16 bytes of chunk position l % 32 of row 2Aw + 2h + l / 32.  Rows at or past the
+  // tile's row count repeat its last row (their MFMA columns are discarded).
   const int64_t arows = GU ? p.T : p.S;
   const __amdgpu_buffer_rsrc_t ares = rsrc(p.a, uint32_t(arows * p.K * 2));
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < kActLoads; ++h) {
     // the two rows of this load are wave-uniform, so their sources come from scalar loads
-    const int c0 = 4 * wave + 2 * h, c1 = c0 + 1;
+    const int c0 = 2 * kActLoads * wave + 2 * h, c1 = c0 + 1;
     const int cs0 = c0 < st.rows ? c0 : st.rows - 1, cs1 = c1 < st.rows ? c1 : st.rows - 1;
     const int32_t src0 = GU ? pt.slots[st.row0 + cs0] / p.k_top : st.row0 + cs0;
     const int32_t src1 = GU ? pt.slots[st.row0 + cs1] / p.k_top : st.row0 + cs1;
@@ -178,11 +182,11 @@ __device__ __forceinline__ void issue_step(const GemvArgs& p, const Ptrs& pt,
   }
 }
 
-__device__ __forceinline__ void stage_acts(const u32x4 (&av)[2], int wave, int lane,
+__device__ __forceinline__ void stage_acts(const u32x4 (&av)[kActLoads], int wave, int lane,
                                            uint8_t* xbuf) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int c = 4 * wave + 2 * h + (lane >> 5);
+  for (int h = 0; h < kActLoads; ++h) {
+    const int c = 2 * kActLoads * wave + 2 * h + (lane >> 5);
     *reinterpret_cast<u32x4*>(xbuf + c * kActRowBytes + 16 * (lane & 31)) = av[h];
   }
 }
@@ -354,16 +358,6 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
-#define E4B_GEMV_INST(FMT, GU, RB)                                                  \
-  template __global__ void moe_gemv_kernel<FMT, GU, RB>(                             \
-      GemvArgs, const int32_t*, const int32_t*, const int32_t*, void*);
-#define E4B_GEMV_INST_RB(FMT, GU) \
-  E4B_GEMV_INST(FMT, GU, 1) E4B_GEMV_INST(FMT, GU, 2) E4B_GEMV_INST(FMT, GU, 4)
-E4B_GEMV_INST_RB(0, true)
-E4B_GEMV_INST_RB(0, false)
-E4B_GEMV_INST_RB(1, true)
-E4B_GEMV_INST_RB(1, false)
-
 int cu_count() {
   static int cached[64] = {0};
   int dev = 0;
@@ -392,8 +386,8 @@ hipError_t launch_rb(const GemvArgs& g, const MoeLaunch& L, void* out, int64_t n
   return hipGetLastError();
 }
 
-// Row blocks per wave: the largest of 4, 2, 1 that still gives every resident workgroup an
-// item (the tile count is a device value; its host-side upper bound is used).
+// Row blocks per wave: the largest of kMaxRB, ..., 2, 1 that still gives every resident
+// workgroup an item (the tile count is a device value; its host-side upper bound is used).
 template <int FMT, bool GU>
 hipError_t launch_stage(const GemvArgs& g, const MoeLaunch& L, void* out, int64_t n_out,
                         hipStream_t stream) {
@@ -403,7 +397,9 @@ hipError_t launch_stage(const GemvArgs& g, const MoeLaunch& L, void* out, int64_
     const int64_t per_item = kWaves * rb * per_block;
     return L.max_mtiles * ((n_out + per_item - 1) / per_item);
   };
-  if (items(4) >= wgs) return launch_rb<FMT, GU, 4>(g, L, out, n_out, wgs, stream);
+  if constexpr (kMaxRB >= 4) {
+    if (items(4) >= wgs) return launch_rb<FMT, GU, 4>(g, L, out, n_out, wgs, stream);
+  }
   if (items(2) >= wgs) return launch_rb<FMT, GU, 2>(g, L, out, n_out, wgs, stream);
   return launch_rb<FMT, GU, 1>(g, L, out, n_out, wgs, stream);
 }
