@@ -64,7 +64,7 @@ Tile pick_tile(const e4b_moe_args* a) {
 struct FwdLayout {
   int bm, waves, gemv;
   int64_t max_mtiles;
-  size_t off_x16, off_h, off_y, off_inv, off_tiles, off_n, total;
+  size_t off_x16, off_h, off_y, off_inv, off_tok, off_tiles, off_n, total;
 };
 
 int layout_forward(const e4b_moe_args* a, FwdLayout* L) {
@@ -83,6 +83,8 @@ int layout_forward(const e4b_moe_args* a, FwdLayout* L) {
   L->off_y = off;
   off += align_up(size_t(S) * size_t(a->H) * 4);
   L->off_inv = off;
+  off += align_up(size_t(S) * 4);
+  L->off_tok = off;
   off += align_up(size_t(S) * 4);
   L->off_tiles = off;
   off += align_up(size_t(L->max_mtiles) * 16);
@@ -230,6 +232,7 @@ int e4b_moe_forward(const e4b_moe_args* a, void* stream) {
   M.h = reinterpret_cast<_Float16*>(ws + L.off_h);
   M.y = reinterpret_cast<float*>(ws + L.off_y);
   M.inv = reinterpret_cast<int32_t*>(ws + L.off_inv);
+  M.tok = reinterpret_cast<int32_t*>(ws + L.off_tok);
   M.tiles = reinterpret_cast<int32_t*>(ws + L.off_tiles);
   M.n_mtiles = reinterpret_cast<int32_t*>(ws + L.off_n);
   M.events = a->stage_events;

@@ -50,6 +50,7 @@ struct MoeLaunch {
   _Float16* h;     // [S, I]
   float* y;        // [S, H], sorted-row order
   int32_t* inv;    // [S]: slot -> sorted row
+  int32_t* tok;    // [S]: sorted row -> token (slot / k)
   int32_t* tiles;  // [max_mtiles, 4]
   int32_t* n_mtiles;
   void* const* events;  // nullable: 6 hipEvent_t around the 5 stages

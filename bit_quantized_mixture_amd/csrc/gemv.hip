@@ -65,7 +65,6 @@ struct GemvArgs {
   int64_t N;               // weight rows per expert (2I for gate_up, H for down)
   int64_t I;
   int64_t T, S;            // tokens, routed rows (rows of x16 and of h)
-  int32_t k_top;
   int32_t n_rblocks;       // weight-row blocks per expert
 };
 
@@ -74,7 +73,7 @@ struct GemvArgs {
 // count against the vector-memory counter the pipeline waits on.
 struct Ptrs {
   const int32_t* __restrict__ tiles;  // [n, 4]: expert, first sorted row, rows (<= 16), 0
-  const int32_t* __restrict__ slots;  // sorted slots [S]
+  const int32_t* __restrict__ tok;    // token of each sorted row [S]
   void* __restrict__ out;             // gate_up: h fp16 [S, I]; down: y float [S, N] (sorted)
 };
 
@@ -85,18 +84,41 @@ struct StepInfo {
   bool last;      // last step of its item
 };
 
-__device__ __forceinline__ StepInfo step_info(const GemvArgs& p, const Ptrs& q, int s, int nseg) {
+// Position of the next step a workgroup issues: flat step s (held at the workgroup's last
+// step once reached), K segment seg of item (tile mt, row block rb).  Items of a workgroup
+// are blockIdx + i * gridDim, so moving to the next item adds fixed amounts to (mt, rb) and
+// no division runs per step.
+struct Cursor {
+  int32_t s, seg, mt, rb;
+};
+
+struct CursorStride {
+  int32_t last, nseg, n_rblocks, d_mt, d_rb;
+};
+
+__device__ __forceinline__ void advance(Cursor& c, const CursorStride& d) {
+  if (c.s < d.last) {
+    ++c.s;
+    if (++c.seg == d.nseg) {
+      c.seg = 0;
+      c.mt += d.d_mt;
+      c.rb += d.d_rb;
+      if (c.rb >= d.n_rblocks) {
+        c.rb -= d.n_rblocks;
+        ++c.mt;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ StepInfo step_at(const Ptrs& q, const Cursor& c, int nseg) {
   StepInfo st;
-  const int it = s / nseg;
-  const int item = int(blockIdx.x) + it * int(gridDim.x);
-  const int seg = s - it * nseg;
-  const int mt = item / p.n_rblocks;
-  st.rb = item - mt * p.n_rblocks;
-  st.e = q.tiles[4 * mt];
-  st.row0 = q.tiles[4 * mt + 1];
-  st.rows = q.tiles[4 * mt + 2];
-  st.kstep = seg * kStepK;
-  st.last = seg == nseg - 1;
+  st.rb = c.rb;
+  st.e = q.tiles[4 * c.mt];
+  st.row0 = q.tiles[4 * c.mt + 1];
+  st.rows = q.tiles[4 * c.mt + 2];
+  st.kstep = c.seg * kStepK;
+  st.last = c.seg == nseg - 1;
   return st;
 }
 
@@ -135,7 +157,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 }
 
 // Issue every memory operation of one step, all unconditional, so the count per step is the
-// same for every wave.  Pieces past K read the next row (or zeros past the buffer); their
+// same for every wave.  The activations go first: the workgroup barrier of a step waits only
+// for them, and each wave waits for its own weights where it first uses them.  Pieces past K read the next row (or zeros past the buffer); their
 // scale is forced to 0 where the data are used, and activation columns past K meet zero
 // weights.
 template <int FMT, bool GU, int RB>
@@ -151,17 +174,6 @@ __device__ __forceinline__ void issue_step(const GemvArgs& p, const Ptrs& pt,
       rsrc(reinterpret_cast<const uint8_t*>(p.sc) + int64_t(st.e) * p.N * nbs, uint32_t(p.N) * nbs);
   const int wso = st.kstep >> 1;                               // uniform byte offsets of the step
   const int sso = FMT == 0 ? (st.kstep >> 6) * 4 : (st.kstep >> 5);
-#pragma unroll
-  for (int b = 0; b < RB; ++b) {
-    const uint32_t row = uint32_t(lane_row<GU, RB>(p, st.rb, wave, b, r));
-    const uint32_t wo = row * kb + 32 * g;
-    R.w[b][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, wo, wso, 0));
-    R.w[b][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, wo + 16, wso, 0));
-    if (FMT == 0)
-      R.sv[b] = __builtin_amdgcn_raw_buffer_load_b32(sres, row * nbs + 4 * g, sso, 0);
-    else
-      R.sv[b] = __builtin_amdgcn_raw_buffer_load_b16(sres, row * nbs + 2 * g, sso, 0);
-  }
   // activations: 16 rows x 512 B; wave w loads rows 2Aw .. 2Aw + 2A - 1 (A = kActLoads), lane
   // l the 16 bytes of chunk position l % 32 of row 2Aw + 2h + l / 32.  Rows at or past the
   // tile's row count repeat its last row (their MFMA columns are discarded).
@@ -172,13 +184,24 @@ __device__ __forceinline__ void issue_step(const GemvArgs& p, const Ptrs& pt,
     // the two rows of this load are wave-uniform, so their sources come from scalar loads
     const int c0 = 2 * kActLoads * wave + 2 * h, c1 = c0 + 1;
     const int cs0 = c0 < st.rows ? c0 : st.rows - 1, cs1 = c1 < st.rows ? c1 : st.rows - 1;
-    const int32_t src0 = GU ? pt.slots[st.row0 + cs0] / p.k_top : st.row0 + cs0;
-    const int32_t src1 = GU ? pt.slots[st.row0 + cs1] / p.k_top : st.row0 + cs1;
+    const int32_t src0 = GU ? pt.tok[st.row0 + cs0] : st.row0 + cs0;
+    const int32_t src1 = GU ? pt.tok[st.row0 + cs1] : st.row0 + cs1;
     const int c = (lane >> 5) ? c1 : c0;
     const uint32_t src = uint32_t((lane >> 5) ? src1 : src0);
     const uint32_t ao = src * uint32_t(p.K * 2) + 16 * uint32_t(xpos(c, lane & 31));
     R.av[h] = __builtin_bit_cast(u32x4,
                                  __builtin_amdgcn_raw_buffer_load_b128(ares, ao, st.kstep * 2, 0));
+  }
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const uint32_t row = uint32_t(lane_row<GU, RB>(p, st.rb, wave, b, r));
+    const uint32_t wo = row * kb + 32 * g;
+    R.w[b][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, wo, wso, 0));
+    R.w[b][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, wo + 16, wso, 0));
+    if (FMT == 0)
+      R.sv[b] = __builtin_amdgcn_raw_buffer_load_b32(sres, row * nbs + 4 * g, sso, 0);
+    else
+      R.sv[b] = __builtin_amdgcn_raw_buffer_load_b16(sres, row * nbs + 2 * g, sso, 0);
   }
 }
 
@@ -284,11 +307,13 @@ __device__ __forceinline__ void store_block(const GemvArgs& p, const Ptrs& pt,
 template <int FMT, bool GU, int RB>
 __global__ void __launch_bounds__(kThreads)
     moe_gemv_kernel(GemvArgs p, const int32_t* __restrict__ tiles,
-                    const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ slots,
+                    const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ tok,
                     void* __restrict__ out) {
-  const Ptrs pt{tiles, slots, out};
+  const Ptrs pt{tiles, tok, out};
   constexpr int kLut = FMT == 0 ? kLutBytes : 0;
   constexpr int kOps = ops_per_step<RB>();
+  constexpr int kActWait = (kStages - 1) * kOps + 3 * RB;  // loads issued after a step's acts
+  static_assert(kActWait < 64, "vmcnt range");
   constexpr int NA = RB < 2 ? 2 : RB;  // accumulators (two alternating chains when RB == 1)
   // one allocation: the table, then two activation buffers
   __shared__ __attribute__((aligned(16))) uint8_t smem[kLut + 2 * kActBufBytes];
@@ -306,7 +331,8 @@ __global__ void __launch_bounds__(kThreads)
   if (FMT == 0) nf4_lut_fill(lut, tid, kThreads);
 
   // Ring of kStages register sets: step s uses set s % kStages and LDS buffer s % 2; the loads
-  // of steps s + 1 .. s + kStages - 1 are in flight while step s is computed.  Past the last
+  // of steps s + 1 .. s + kStages - 1 (and step s's own weights, until first used) are in
+  // flight while step s is computed.  Past the last
   // step the loads repeat it and are never used.  Step s's activations are written to LDS
   // right before its barrier, and the barrier of step s + 1 also tells that every wave is done
   // reading buffer s % 2, so one barrier per step suffices.  The loop has a single exit so the
@@ -318,37 +344,44 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
   for (int a = 0; a < NA; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  const int first = int(blockIdx.x);
+  Cursor cur{0, 0, first / p.n_rblocks, first % p.n_rblocks};
+  const CursorStride cst{last, nseg, p.n_rblocks, int(gridDim.x) / p.n_rblocks,
+                         int(gridDim.x) % p.n_rblocks};
 #pragma unroll
   for (int b = 0; b < kStages - 1; ++b) {
-    ci[b] = step_info(p, pt, b < last ? b : last, nseg);
+    ci[b] = step_at(pt, cur, nseg);
     issue_step<FMT, GU, RB>(p, pt, ci[b], wave, lane, R[b]);
+    advance(cur, cst);
   }
   constexpr int kPeriod = kStages % 2 ? 2 * kStages : kStages;  // (register set, LDS buffer)
   for (int s = 0; s < nsteps; s += kPeriod) {
 #pragma unroll
     for (int b2 = 0; b2 < kPeriod; ++b2) {
-      const int cur = b2 % kStages, nxt = (b2 + kStages - 1) % kStages;
-      const int sn = s + b2 + kStages - 1;
+      const int rs = b2 % kStages, nxt = (b2 + kStages - 1) % kStages;
       uint8_t* const xbuf = smem + kLut + (b2 & 1) * kActBufBytes;
-      ci[nxt] = step_info(p, pt, sn < last ? sn : last, nseg);
+      // step min(s + b2 + kStages - 1, last)
+      ci[nxt] = step_at(pt, cur, nseg);
       issue_step<FMT, GU, RB>(p, pt, ci[nxt], wave, lane, R[nxt]);
-      // step s + b2 has landed for this wave (later steps' loads may stay in flight) ...
+      advance(cur, cst);
+      // the activations of step s + b2 have landed for this wave (its weights and the later
+      // steps' loads may stay in flight) ...
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((kStages - 1) * kOps));
-      stage_acts(R[cur].av, wave, lane, xbuf);
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0((kStages - 1) * kOps));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kActWait));
+      stage_acts(R[rs].av, wave, lane, xbuf);
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kActWait));
       // ... and for every wave, with its activations (and the table) in LDS
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       if (b2 == 0 || s + b2 < nsteps) {
-        compute_step<FMT, RB, NA>(p.K - ci[cur].kstep, lane, R[cur], xbuf, lut, acc);
-        if (ci[cur].last) {
+        compute_step<FMT, RB, NA>(p.K - ci[rs].kstep, lane, R[rs], xbuf, lut, acc);
+        if (ci[rs].last) {
           if (RB == 1) {
-            store_block<GU, RB>(p, pt, ci[cur], wave, lane, 0, acc[0] + acc[1]);
+            store_block<GU, RB>(p, pt, ci[rs], wave, lane, 0, acc[0] + acc[1]);
           } else {
 #pragma unroll
             for (int b = 0; b < RB; ++b)
-              store_block<GU, RB>(p, pt, ci[cur], wave, lane, b, acc[b]);
+              store_block<GU, RB>(p, pt, ci[rs], wave, lane, b, acc[b]);
           }
 #pragma unroll
           for (int a = 0; a < NA; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -382,7 +415,7 @@ hipError_t launch_rb(const GemvArgs& g, const MoeLaunch& L, void* out, int64_t n
   int64_t grid = wgs < max_items ? wgs : max_items;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL((moe_gemv_kernel<FMT, GU, RB>), dim3(unsigned(grid)), dim3(kThreads), 0,
-                     stream, a, L.tiles, L.n_mtiles, L.slots, out);
+                     stream, a, L.tiles, L.n_mtiles, L.tok, out);
   return hipGetLastError();
 }
 
@@ -409,7 +442,6 @@ hipError_t launch_stage(const GemvArgs& g, const MoeLaunch& L, void* out, int64_
 template <int FMT>
 static hipError_t launch_gemv_fmt(const MoeLaunch& L, hipStream_t stream, int stage) {
   GemvArgs g{};
-  g.k_top = L.k;
   g.I = L.I;
   g.T = L.T;
   g.S = L.T * L.k;

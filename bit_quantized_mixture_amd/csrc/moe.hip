@@ -353,18 +353,25 @@ E4B_GEMM_INST_ALL(0)
 E4B_GEMM_INST_ALL(1)
 
 // x bf16 -> fp16 (exact for |x| in fp16's normal range), stored in the k-slot order of the
-// weight format inside each aligned group of 8.  Also inverts the routing permutation:
-// inv[slots[p]] = p for the S sorted rows p.
+// weight format inside each aligned group of 8.  Also inverts the routing permutation,
+// inv[slots[p]] = p for the S sorted rows p, and records each sorted row's token,
+// tok[p] = slots[p] / k.
 template <int FMT>
 __global__ void __launch_bounds__(256) convert_x_kernel(const uint16_t* __restrict__ x,
                                                         _Float16* __restrict__ x16,
                                                         int64_t n_chunks,
                                                         const int32_t* __restrict__ slots,
-                                                        int64_t S, int32_t* __restrict__ inv) {
+                                                        int64_t S, int32_t k,
+                                                        int32_t* __restrict__ inv,
+                                                        int32_t* __restrict__ tok) {
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   const int64_t n = n_chunks > S ? n_chunks : S;
   for (int64_t q = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; q < n; q += stride) {
-    if (q < S) inv[slots[q]] = int32_t(q);
+    if (q < S) {
+      const int32_t sl = slots[q];
+      inv[sl] = int32_t(q);
+      tok[q] = sl / k;
+    }
     if (q >= n_chunks) continue;
     const u32x4 raw = *reinterpret_cast<const u32x4*>(x + 8 * q);
     _Float16 v[8];
@@ -499,10 +506,10 @@ static hipError_t launch_fmt(const MoeLaunch& L, hipStream_t stream) {
   const unsigned gx = grid_1d(nchunks > S ? nchunks : S);
   if (FMT == 0 && !L.cfg.gemv)
     hipLaunchKernelGGL(convert_x_kernel<0>, dim3(gx), dim3(256), 0, stream, L.x, L.x16, nchunks,
-                       L.slots, S, L.inv);
+                       L.slots, S, L.k, L.inv, L.tok);
   else
     hipLaunchKernelGGL(convert_x_kernel<1>, dim3(gx), dim3(256), 0, stream, L.x, L.x16, nchunks,
-                       L.slots, S, L.inv);
+                       L.slots, S, L.k, L.inv, L.tok);
   record(L, 1, stream);
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, stream, L.offsets, int(L.E),
                      L.cfg.bm, L.tiles, L.n_mtiles);
