@@ -63,7 +63,8 @@ Tile pick_tile(const e4b_moe_args* a) {
 
 struct FwdLayout {
   int bm, waves, gemv;
-  int64_t max_mtiles;
+  int64_t max_mtiles, max_stiles;
+  int tail_rows;
   size_t off_x16, off_h, off_y, off_inv, off_tok, off_tiles, off_n, total;
 };
 
@@ -75,6 +76,10 @@ int layout_forward(const e4b_moe_args* a, FwdLayout* L) {
   L->gemv = t.gemv;
   const int64_t n_active_max = a->E < S ? a->E : S;
   L->max_mtiles = (S + n_active_max * (L->bm - 1)) / L->bm;
+  // MFMA tiles of 128 or 256 rows: an expert's remainder of at most bm / 4 rows goes to
+  // 32-row tiles (at most bm / 128 of them) instead of a mostly empty full tile
+  L->tail_rows = (!L->gemv && L->bm >= 128) ? L->bm / 4 : 0;
+  L->max_stiles = n_active_max * int64_t((L->tail_rows + 31) / 32);
   size_t off = 0;
   L->off_x16 = off;
   off += align_up(size_t(a->T) * size_t(a->H) * 2);
@@ -87,7 +92,7 @@ int layout_forward(const e4b_moe_args* a, FwdLayout* L) {
   L->off_tok = off;
   off += align_up(size_t(S) * 4);
   L->off_tiles = off;
-  off += align_up(size_t(L->max_mtiles) * 16);
+  off += align_up(size_t(L->max_mtiles + L->max_stiles) * 16);
   L->off_n = off;
   off += kAlign;
   L->total = off;
@@ -218,6 +223,8 @@ int e4b_moe_forward(const e4b_moe_args* a, void* stream) {
   M.cfg.waves = L.waves;
   M.cfg.gemv = L.gemv;
   M.max_mtiles = L.max_mtiles;
+  M.max_stiles = L.max_stiles;
+  M.tail_rows = L.tail_rows;
   M.x = a->x;
   M.w_gu = a->w_gu;
   M.s_gu = a->s_gu;

@@ -35,6 +35,8 @@ struct MoeLaunch {
   int k;
   TileCfg cfg;
   int64_t max_mtiles;
+  int64_t max_stiles;  // bound on 32-row tail tiles (0: not used)
+  int tail_rows;       // an expert's last rows go to 32-row tiles if at most this many
   const uint16_t* x;
   const uint8_t* w_gu;
   const void* s_gu;
@@ -51,8 +53,8 @@ struct MoeLaunch {
   float* y;        // [S, H], sorted-row order
   int32_t* inv;    // [S]: slot -> sorted row
   int32_t* tok;    // [S]: sorted row -> token (slot / k)
-  int32_t* tiles;  // [max_mtiles, 4]
-  int32_t* n_mtiles;
+  int32_t* tiles;  // [max_mtiles + max_stiles, 4]: main tiles, then tail tiles
+  int32_t* n_mtiles;  // [2]: main and tail tile counts
   void* const* events;  // nullable: 6 hipEvent_t around the 5 stages
 };
 

@@ -387,36 +387,51 @@ __global__ void __launch_bounds__(256) convert_x_kernel(const uint16_t* __restri
   }
 }
 
-// One workgroup: walk the experts in order, cut each expert's rows into BM-row tiles.
+// Exclusive prefix sum of v over the 256 threads of the workgroup; *total = the sum.
+__device__ __forceinline__ int block_exclusive_scan(int v, int32_t* wsum, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  __syncthreads();
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int woff = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    woff += w < wave ? wsum[w] : 0;
+    tot += wsum[w];
+  }
+  *total = tot;
+  return woff + incl - v;
+}
+
+// One workgroup: walk the experts in order and cut each expert's rows into bm-row tiles.  If
+// the last piece of an expert has at most `tail` rows (tail > 0), it is cut into 32-row
+// tiles instead, listed in tails[] (their count in n_mtiles[1]), so a full-size tile is not
+// spent on a few rows.
 __global__ void __launch_bounds__(256) build_tiles_kernel(const int32_t* __restrict__ offsets,
-                                                          int E, int bm,
+                                                          int E, int bm, int tail,
                                                           int32_t* __restrict__ tiles,
+                                                          int32_t* __restrict__ tails,
                                                           int32_t* __restrict__ n_mtiles) {
   __shared__ int32_t wsum[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int run = 0;
+  const int tid = threadIdx.x;
+  int run = 0, run_s = 0;
   for (int base = 0; base < E; base += 256) {
     const int e = base + tid;
     const int start = e < E ? offsets[e] : 0;
     const int cnt = e < E ? offsets[e + 1] - start : 0;
-    const int nt = (cnt + bm - 1) / bm;
-    // inclusive scan inside the wave
-    int incl = nt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
-    __syncthreads();
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    int woff = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      woff += w < wave ? wsum[w] : 0;
-      tot += wsum[w];
-    }
-    const int first = run + woff + incl - nt;
+    const int nfull = cnt / bm, rem = cnt - nfull * bm;
+    const bool split = rem > 0 && rem <= tail;
+    const int nt = split ? nfull : (cnt + bm - 1) / bm;
+    const int ns = split ? (rem + 31) / 32 : 0;
+    int tot, tot_s;
+    const int first = run + block_exclusive_scan(nt, wsum, &tot);
+    const int first_s = run_s + block_exclusive_scan(ns, wsum, &tot_s);
     for (int i = 0; i < nt; ++i) {
       int32_t* t = tiles + 4 * int64_t(first + i);
       t[0] = e;
@@ -424,9 +439,20 @@ __global__ void __launch_bounds__(256) build_tiles_kernel(const int32_t* __restr
       t[2] = min(bm, cnt - i * bm);
       t[3] = 0;
     }
+    for (int i = 0; i < ns; ++i) {
+      int32_t* t = tails + 4 * int64_t(first_s + i);
+      t[0] = e;
+      t[1] = start + nfull * bm + 32 * i;
+      t[2] = min(32, rem - 32 * i);
+      t[3] = 0;
+    }
     run += tot;
+    run_s += tot_s;
   }
-  if (tid == 0) *n_mtiles = run;
+  if (tid == 0) {
+    n_mtiles[0] = run;
+    n_mtiles[1] = run_s;
+  }
 }
 
 // out[t, :] = sum_{j<k} topk_w[s] * y[inv[s], :] with s = t*k + j, fixed order; fp32 and
@@ -465,11 +491,28 @@ static void record(const MoeLaunch& L, int i, hipStream_t stream) {
   if (L.events) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(L.events[i]), stream);
 }
 
+// One grouped GEMM stage over the main tiles, then over the 32-row tail tiles if any.
+template <int FMT, bool GU, int BM, int WAVES>
+static void launch_stage_tiles(const MoeLaunch& L, GemmArgs g, hipStream_t stream) {
+  const int64_t n_out = GU ? L.I : L.H;
+  const int per_wave = GU ? 32 : 64;
+  g.tiles = L.tiles;
+  g.n_mtiles = L.n_mtiles;
+  g.n_ntiles = int((n_out + WAVES * per_wave - 1) / (WAVES * per_wave));
+  hipLaunchKernelGGL((moe_gemm_kernel<FMT, GU, BM, WAVES>),
+                     dim3(unsigned(L.max_mtiles * g.n_ntiles)), dim3(WAVES * 64), 0, stream, g);
+  if (BM != 32 && L.max_stiles > 0) {
+    g.tiles = L.tiles + 4 * L.max_mtiles;
+    g.n_mtiles = L.n_mtiles + 1;
+    g.n_ntiles = int((n_out + per_wave - 1) / per_wave);
+    hipLaunchKernelGGL((moe_gemm_kernel<FMT, GU, 32, 1>),
+                       dim3(unsigned(L.max_stiles * g.n_ntiles)), dim3(64), 0, stream, g);
+  }
+}
+
 template <int FMT, int BM, int WAVES>
 static hipError_t launch_gemms(const MoeLaunch& L, hipStream_t stream) {
   GemmArgs g{};
-  g.tiles = L.tiles;
-  g.n_mtiles = L.n_mtiles;
   g.slots = L.slots;
   g.k_top = L.k;
   g.I = L.I;
@@ -481,9 +524,7 @@ static hipError_t launch_gemms(const MoeLaunch& L, hipStream_t stream) {
   g.out = L.h;
   g.K = L.H;
   g.N = 2 * L.I;
-  g.n_ntiles = int((L.I + WAVES * 32 - 1) / (WAVES * 32));
-  hipLaunchKernelGGL((moe_gemm_kernel<FMT, true, BM, WAVES>),
-                     dim3(unsigned(L.max_mtiles * g.n_ntiles)), dim3(WAVES * 64), 0, stream, g);
+  launch_stage_tiles<FMT, true, BM, WAVES>(L, g, stream);
   record(L, 3, stream);
   // down + routing weight
   g.a = L.h;
@@ -492,9 +533,7 @@ static hipError_t launch_gemms(const MoeLaunch& L, hipStream_t stream) {
   g.out = L.y;
   g.K = L.I;
   g.N = L.H;
-  g.n_ntiles = int((L.H + WAVES * 64 - 1) / (WAVES * 64));
-  hipLaunchKernelGGL((moe_gemm_kernel<FMT, false, BM, WAVES>),
-                     dim3(unsigned(L.max_mtiles * g.n_ntiles)), dim3(WAVES * 64), 0, stream, g);
+  launch_stage_tiles<FMT, false, BM, WAVES>(L, g, stream);
   return hipGetLastError();
 }
 
@@ -512,7 +551,7 @@ static hipError_t launch_fmt(const MoeLaunch& L, hipStream_t stream) {
                        L.slots, S, L.k, L.inv, L.tok);
   record(L, 1, stream);
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, stream, L.offsets, int(L.E),
-                     L.cfg.bm, L.tiles, L.n_mtiles);
+                     L.cfg.bm, L.tail_rows, L.tiles, L.tiles + 4 * L.max_mtiles, L.n_mtiles);
   record(L, 2, stream);
   hipError_t err;
   if (L.cfg.gemv) {

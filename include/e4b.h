@@ -63,7 +63,8 @@ typedef enum e4b_fmt { E4B_FMT_NF4 = 0, E4B_FMT_MXFP4 = 1 } e4b_fmt;
  * when the mean routed rows per expert T*k/E is below 16, the MFMA tile path otherwise.
  * The choice depends only on host-known sizes; no device value is read back. */
 #define E4B_PATH_AUTO 0x0
-#define E4B_PATH_GEMM 0x1 /* MFMA grouped GEMM, 128- or 256-row tiles */
+#define E4B_PATH_GEMM 0x1 /* MFMA grouped GEMM, 128- or 256-row tiles (an expert's last <= 1/4
+                           * tile of rows goes to 32-row tiles) */
 #define E4B_PATH_GEMV 0x2 /* small-M streaming path: 16-row tiles, each expert's weights streamed
                            * once per 16 routed rows */
 #define E4B_PATH_MASK 0x3
