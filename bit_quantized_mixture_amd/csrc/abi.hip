@@ -58,7 +58,7 @@ Tile pick_tile(const e4b_moe_args* a) {
   const double mean_rows = double(S) / double(a->E);
   if (path == E4B_PATH_GEMV || (path == E4B_PATH_AUTO && mean_rows < 16.0))
     return {e4b::kGemvTileRows, 4, 1};
-  return mean_rows >= 512.0 ? Tile{256, 4, 0} : Tile{128, 4, 0};
+  return mean_rows >= 256.0 ? Tile{256, 4, 0} : Tile{128, 4, 0};
 }
 
 struct FwdLayout {

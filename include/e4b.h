@@ -60,8 +60,8 @@ typedef enum e4b_fmt { E4B_FMT_NF4 = 0, E4B_FMT_MXFP4 = 1 } e4b_fmt;
 #define E4B_ROUTE_RENORMALIZE 0x1 /* softmax over the chosen k logits (default reading) */
 
 /* e4b_moe_args.flags: execution path (bits 0-1).  AUTO picks the small-M streaming path
- * when the mean routed rows per expert T*k/E is below 16, the MFMA tile path otherwise.
- * The choice depends only on host-known sizes; no device value is read back. */
+ * when the mean routed rows per expert T*k/E is below 16, the MFMA tile path otherwise
+ * (128-row tiles below a mean of 256 rows, 256-row tiles from there).  The choice depends only on host-known sizes; no device value is read back. */
 #define E4B_PATH_AUTO 0x0
 #define E4B_PATH_GEMM 0x1 /* MFMA grouped GEMM, 128- or 256-row tiles (an expert's last <= 1/4
                            * tile of rows goes to 32-row tiles) */
