@@ -159,7 +159,7 @@ int e4b_pack_mxfp4(const uint16_t* w, int64_t E, int64_t N, int64_t K, uint8_t* 
 int e4b_route_workspace_bytes(int64_t T, int64_t E, int32_t k, size_t* bytes) {
   if (!bytes) return E4B_ERR_ARG;
   if (T < 0 || E <= 0 || k < 1) return E4B_ERR_ARG;
-  *bytes = align_up(size_t(E) * 4);
+  *bytes = align_up(size_t(e4b::route_chunks(T)) * size_t(E) * 4);
   return E4B_OK;
 }
 

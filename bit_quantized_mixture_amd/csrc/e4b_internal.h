@@ -24,9 +24,10 @@ hipError_t launch_pack_nf4(const uint16_t* w, int64_t n_elems, uint8_t* packed, 
 hipError_t launch_pack_mxfp4(const uint16_t* w, int64_t n_elems, uint8_t* blocks, uint8_t* scales,
                              hipStream_t stream);
 
-// Routing: counts (E int32) live in the workspace.
+// Routing: per-(chunk, expert) counts, [route_chunks(T), E] int32, live in the workspace.
+int route_chunks(int64_t T);
 hipError_t launch_route(const float* logits, int64_t T, int64_t E, int k, bool renorm,
-                        int32_t* ids, float* w, int32_t* offsets, int32_t* slots, int32_t* counts,
+                        int32_t* ids, float* w, int32_t* offsets, int32_t* slots, int32_t* cc,
                         hipStream_t stream);
 
 struct MoeLaunch {

@@ -2,23 +2,24 @@
 // and the expert-major, token-ordered slot permutation that groups every expert's rows
 // contiguously for the grouped GEMMs (grouped-nf4-gemm 0.25.0 project description, opening
 // section: one launch over all active experts, a router epilogue among the glue kernels).
+// The permutation is a stable counting sort over chunks of 1024 tokens:
 //
-//   1. zero_counts     counts[E] = 0
-//   2. topk_kernel     one wave per token: k rounds of a wave-wide arg-max under the order
-//                      (higher logit, then lower expert index); softmax weights; counts[e]++
-//   3. scatter_kernel  one workgroup per expert: its offset is the sum of the counts of the
-//                      lower experts; tokens are scanned in order with a ballot prefix sum,
-//                      so slots land expert-major and token-ascending (stable, deterministic)
+//   1. topk_kernel     one wave per token: k rounds of a wave-wide arg-max under the order
+//                      (higher logit, then lower expert index); softmax weights
+//   2. count_kernel    one workgroup per chunk: LDS histogram of the chunk's picks, cc[c][e]
+//                      (no global atomics: per-pick atomics on a few hot counters serialised
+//                      badly, 80 us at T = 4096, E = 8)
+//   3. offsets_kernel  one workgroup: expert offsets (prefix sum of the totals) and the first
+//                      slot of every (chunk, expert) pair
+//   4. scatter_kernel  one workgroup per (chunk, expert): the chunk's tokens in order with a
+//                      ballot prefix sum, so slots land expert-major and token-ascending
+//                      (stable, deterministic)
 #include "e4b_device.h"
 #include "e4b_internal.h"
 
 namespace e4b {
 
 constexpr int kMaxExpertsPerLane = 16;  // E <= 1024
-
-__global__ void zero_counts_kernel(int32_t* __restrict__ p, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
-}
 
 // a beats b: higher value, or equal value and lower index.  Invalid entries carry
 // index INT_MAX and value -inf; logits are finite, so any valid entry beats them.
@@ -29,8 +30,7 @@ __device__ __forceinline__ bool beats(float va, int ia, float vb, int ib) {
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int64_t T,
                                                    int E, int k, int renorm,
                                                    int32_t* __restrict__ ids,
-                                                   float* __restrict__ wts,
-                                                   int32_t* __restrict__ counts) {
+                                                   float* __restrict__ wts) {
   const int lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave exits together
@@ -89,35 +89,91 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   if (lane < k) {
     ids[t * k + lane] = my_id;
     wts[t * k + lane] = ex / denom;
-    atomicAdd(&counts[my_id], 1);
   }
 }
 
+constexpr int kTokChunk = 1024;  // tokens per chunk of the counting sort
+
+int route_chunks(int64_t T) { return int(T > 0 ? (T + kTokChunk - 1) / kTokChunk : 1); }
+
+// cc[c][e] = number of picks of expert e by the tokens of chunk c (LDS histogram).
+__global__ void __launch_bounds__(256) count_kernel(const int32_t* __restrict__ ids, int64_t T,
+                                                    int E, int k, int32_t* __restrict__ cc) {
+  __shared__ int32_t hist[1024];
+  for (int i = threadIdx.x; i < E; i += 256) hist[i] = 0;
+  __syncthreads();
+  const int64_t lo = int64_t(blockIdx.x) * kTokChunk * k;
+  int64_t hi = lo + int64_t(kTokChunk) * k;
+  if (hi > T * k) hi = T * k;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += 256) atomicAdd(&hist[ids[i]], 1);
+  __syncthreads();
+  for (int i = threadIdx.x; i < E; i += 256) cc[int64_t(blockIdx.x) * E + i] = hist[i];
+}
+
+// One workgroup: offsets[e] = exclusive prefix sum over experts of the total counts,
+// offsets[E] = T*k; then cc[c][e] becomes the first slot of (chunk c, expert e):
+// offsets[e] + sum of cc[c'][e] over c' < c.
+__global__ void __launch_bounds__(256) offsets_kernel(int32_t* __restrict__ cc, int chunks, int E,
+                                                      int32_t* __restrict__ offsets) {
+  __shared__ int32_t wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int kPer = 4;  // experts per thread (E <= 1024)
+  int tot[kPer];
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = tid * kPer + i;
+    int t = 0;
+    if (e < E)
+      for (int c = 0; c < chunks; ++c) t += cc[int64_t(c) * E + e];
+    tot[i] = t;
+    mine += t;
+  }
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int run = incl - mine;
+  for (int w = 0; w < wave; ++w) run += wsum[w];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = tid * kPer + i;
+    if (e < E) {
+      offsets[e] = run;
+      int base = run;
+      for (int c = 0; c < chunks; ++c) {
+        const int v = cc[int64_t(c) * E + e];
+        cc[int64_t(c) * E + e] = base;
+        base += v;
+      }
+    }
+    run += tot[i];
+  }
+  if (tid == 255) offsets[E] = run;
+}
+
+// One workgroup per (chunk c, expert e): the chunk's tokens in order, with a ballot prefix
+// sum, so the slots of e land token-ascending from cc[c][e].
 __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict__ ids, int64_t T,
                                                       int E, int k,
-                                                      const int32_t* __restrict__ counts,
-                                                      int32_t* __restrict__ offsets,
+                                                      const int32_t* __restrict__ cc,
                                                       int32_t* __restrict__ slots) {
-  __shared__ int32_t red[4];
   __shared__ int32_t wave_tot[4];
-  const int e = blockIdx.x;
+  const int e = int(blockIdx.x % unsigned(E));
+  const int64_t c = blockIdx.x / unsigned(E);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int part = 0;
-  for (int i = tid; i < e; i += 256) part += counts[i];
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) part += __shfl_xor(part, off);
-  if (lane == 0) red[wave] = part;
-  __syncthreads();
-  const int base = red[0] + red[1] + red[2] + red[3];
-  if (tid == 0) {
-    offsets[e] = base;
-    if (e == E - 1) offsets[E] = base + counts[e];
-  }
+  const int base = cc[c * E + e];
+  int64_t t_end = (c + 1) * kTokChunk;
+  if (t_end > T) t_end = T;
   int running = 0;
-  for (int64_t t0 = 0; t0 < T; t0 += 256) {
+  for (int64_t t0 = c * kTokChunk; t0 < t_end; t0 += 256) {
     const int64_t t = t0 + tid;
     int flag = 0, jsel = 0;
-    if (t < T) {
+    if (t < t_end) {
       for (int j = 0; j < k; ++j) {
         if (ids[t * k + j] == e) {
           flag = 1;
@@ -142,17 +198,20 @@ __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict_
 }
 
 hipError_t launch_route(const float* logits, int64_t T, int64_t E, int k, bool renorm,
-                        int32_t* ids, float* w, int32_t* offsets, int32_t* slots, int32_t* counts,
+                        int32_t* ids, float* w, int32_t* offsets, int32_t* slots, int32_t* cc,
                         hipStream_t stream) {
-  hipLaunchKernelGGL(zero_counts_kernel, dim3(int((E + 255) / 256)), dim3(256), 0, stream, counts,
-                     int(E));
+  const int chunks = route_chunks(T);
   if (T > 0) {
     const int64_t blocks = (T + 3) / 4;
     hipLaunchKernelGGL(topk_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, logits, T,
-                       int(E), k, renorm ? 1 : 0, ids, w, counts);
+                       int(E), k, renorm ? 1 : 0, ids, w);
   }
-  hipLaunchKernelGGL(scatter_kernel, dim3(unsigned(E)), dim3(256), 0, stream, ids, T, int(E), k,
-                     counts, offsets, slots);
+  hipLaunchKernelGGL(count_kernel, dim3(unsigned(chunks)), dim3(256), 0, stream, ids, T, int(E),
+                     k, cc);
+  hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(256), 0, stream, cc, chunks, int(E), offsets);
+  if (T > 0)
+    hipLaunchKernelGGL(scatter_kernel, dim3(unsigned(int64_t(chunks) * E)), dim3(256), 0, stream,
+                       ids, T, int(E), k, cc, slots);
   return hipGetLastError();
 }
 

@@ -40,7 +40,9 @@ def test_route_skewed_has_empty_experts(e4b):
 
 
 @pytest.mark.parametrize("T,E,k", [(1, 1, 1), (5, 1, 1), (1, 8, 8), (33, 8, 8), (1, 128, 8),
-                                   (300, 1024, 64), (70, 65, 3), (257, 16, 2)])
+                                   (300, 1024, 64), (70, 65, 3), (257, 16, 2),
+                                   # several 1024-token chunks of the counting sort, ragged last
+                                   (2500, 1024, 8), (3073, 3, 2), (1024, 7, 7), (1025, 1, 1)])
 def test_route_edge_shapes(e4b, T, E, k):
     rng = np.random.default_rng(T * 1000 + E + k)
     _check(e4b, rng.standard_normal((T, E), dtype=np.float32), k)
