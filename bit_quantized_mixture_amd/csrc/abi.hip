@@ -77,9 +77,9 @@ int layout_forward(const e4b_moe_args* a, FwdLayout* L) {
   const int64_t n_active_max = a->E < S ? a->E : S;
   L->max_mtiles = (S + n_active_max * (L->bm - 1)) / L->bm;
   // MFMA tiles of 128 or 256 rows: an expert's remainder of at most bm / 4 rows goes to
-  // 32-row tiles (at most bm / 128 of them) instead of a mostly empty full tile
+  // 16-row tiles of the streaming kernel instead of a mostly empty full tile
   L->tail_rows = (!L->gemv && L->bm >= 128) ? L->bm / 4 : 0;
-  L->max_stiles = n_active_max * int64_t((L->tail_rows + 31) / 32);
+  L->max_stiles = n_active_max * int64_t((L->tail_rows + e4b::kGemvTileRows - 1) / e4b::kGemvTileRows);
   size_t off = 0;
   L->off_x16 = off;
   off += align_up(size_t(a->T) * size_t(a->H) * 2);

@@ -36,8 +36,8 @@ struct MoeLaunch {
   int k;
   TileCfg cfg;
   int64_t max_mtiles;
-  int64_t max_stiles;  // bound on 32-row tail tiles (0: not used)
-  int tail_rows;       // an expert's last rows go to 32-row tiles if at most this many
+  int64_t max_stiles;  // bound on 16-row tail tiles (0: not used)
+  int tail_rows;       // an expert's last rows go to tail tiles if at most this many
   const uint16_t* x;
   const uint8_t* w_gu;
   const void* s_gu;
@@ -63,5 +63,7 @@ hipError_t launch_moe_forward(const MoeLaunch& L, hipStream_t stream);
 
 // Small-M streaming kernels: stage 0 = gate_up + SwiGLU (x16 -> h), 1 = down (h -> y).
 hipError_t launch_gemv(const MoeLaunch& L, hipStream_t stream, int stage);
+// The same kernels over the tail tiles of the MFMA-tile path (its activation order).
+hipError_t launch_gemv_tails(const MoeLaunch& L, hipStream_t stream, int stage);
 
 }  // namespace e4b

@@ -217,7 +217,7 @@ __device__ __forceinline__ void stage_acts(const u32x4 (&av)[kActLoads], int wav
 // MFMAs of one step as one straight-line block.  Group n = ((i * 4 + q) * RB + b): dword q of
 // load i of row block b.  The table lookups (and, for the first row block, the activation
 // fragment) of group n + 2 are issued before group n is formed.
-template <int FMT, int RB, int NA>
+template <int FMT, int RB, int NA, bool SLOT>
 __device__ __forceinline__ void compute_step(int64_t krem, int lane, const StepRegs<RB>& R,
                                              const uint8_t* xbuf, const uint8_t* lut,
                                              f32x4 (&acc)[NA]) {
@@ -267,6 +267,15 @@ __device__ __forceinline__ void compute_step(int64_t krem, int lane, const StepR
     if (FMT == 0) {
 #pragma unroll
       for (int bt = 0; bt < 4; ++bt) d[bt] = pk_mul_f16(lk[n][bt], s16[b]);
+      if (SLOT) {
+        // natural pairs (0,1) (2,3) (4,5) (6,7) -> the slot order of the MFMA-tile path's
+        // activations: (0,2) (4,6) (1,3) (5,7)
+        const uint32_t p0 = d[0], p1 = d[1], p2 = d[2], p3 = d[3];
+        d[0] = perm(p1, p0, 0x05040100u);
+        d[1] = perm(p3, p2, 0x05040100u);
+        d[2] = perm(p1, p0, 0x07060302u);
+        d[3] = perm(p3, p2, 0x07060302u);
+      }
     } else {
       mxfp4_decode8(R.w[b][i][q], smx[b][i], d);
     }
@@ -279,7 +288,7 @@ __device__ __forceinline__ void compute_step(int64_t krem, int lane, const StepR
 }
 
 // Results of one item.  acc of row block b: element i = D[row 4g + i of the block, token r].
-template <bool GU, int RB>
+template <bool GU, int RB, bool SLOT>
 __device__ __forceinline__ void store_block(const GemvArgs& p, const Ptrs& pt,
                                             const StepInfo& st, int wave, int lane, int b,
                                             const f32x4& acc) {
@@ -295,7 +304,7 @@ __device__ __forceinline__ void store_block(const GemvArgs& p, const Ptrs& pt,
       const int32_t j0 = st.rb * (kWaves * RB * 8) + (wave * RB + b) * 8 + 4 * g;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (j0 + i < int32_t(p.I)) h[j0 + i] = (_Float16)swiglu(acc[i], up[i]);
+        if (j0 + i < int32_t(p.I)) h[act_pos<SLOT ? 0 : 1>(j0 + i)] = (_Float16)swiglu(acc[i], up[i]);
     }
   } else if (r < st.rows) {
     float* y = reinterpret_cast<float*>(pt.out) + int64_t(st.row0 + r) * p.N;
@@ -304,7 +313,7 @@ __device__ __forceinline__ void store_block(const GemvArgs& p, const Ptrs& pt,
   }
 }
 
-template <int FMT, bool GU, int RB>
+template <int FMT, bool GU, int RB, bool SLOT>
 __global__ void __launch_bounds__(kThreads)
     moe_gemv_kernel(GemvArgs p, const int32_t* __restrict__ tiles,
                     const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ tok,
@@ -374,14 +383,14 @@ __global__ void __launch_bounds__(kThreads)
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
       if (b2 == 0 || s + b2 < nsteps) {
-        compute_step<FMT, RB, NA>(p.K - ci[rs].kstep, lane, R[rs], xbuf, lut, acc);
+        compute_step<FMT, RB, NA, SLOT>(p.K - ci[rs].kstep, lane, R[rs], xbuf, lut, acc);
         if (ci[rs].last) {
           if (RB == 1) {
-            store_block<GU, RB>(p, pt, ci[rs], wave, lane, 0, acc[0] + acc[1]);
+            store_block<GU, RB, SLOT>(p, pt, ci[rs], wave, lane, 0, acc[0] + acc[1]);
           } else {
 #pragma unroll
             for (int b = 0; b < RB; ++b)
-              store_block<GU, RB>(p, pt, ci[rs], wave, lane, b, acc[b]);
+              store_block<GU, RB, SLOT>(p, pt, ci[rs], wave, lane, b, acc[b]);
           }
 #pragma unroll
           for (int a = 0; a < NA; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -405,42 +414,52 @@ int cu_count() {
   return cached[dev];
 }
 
-template <int FMT, bool GU, int RB>
-hipError_t launch_rb(const GemvArgs& g, const MoeLaunch& L, void* out, int64_t n_out,
-                     int64_t wgs, hipStream_t stream) {
+// A list of 16-row tiles: the tile array, its device-side count and a host-side bound.
+struct TileList {
+  const int32_t* tiles;
+  const int32_t* n;
+  int64_t max_tiles;
+};
+
+template <int FMT, bool GU, int RB, bool SLOT>
+hipError_t launch_rb(const GemvArgs& g, const TileList& tl, const MoeLaunch& L, void* out,
+                     int64_t n_out, int64_t wgs, hipStream_t stream) {
   constexpr int64_t kPerItem = kWaves * RB * (GU ? 8 : 16);  // output rows (gate_up: j) per item
   GemvArgs a = g;
   a.n_rblocks = int((n_out + kPerItem - 1) / kPerItem);
-  const int64_t max_items = L.max_mtiles * a.n_rblocks;
+  const int64_t max_items = tl.max_tiles * a.n_rblocks;
   int64_t grid = wgs < max_items ? wgs : max_items;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL((moe_gemv_kernel<FMT, GU, RB>), dim3(unsigned(grid)), dim3(kThreads), 0,
-                     stream, a, L.tiles, L.n_mtiles, L.tok, out);
+  hipLaunchKernelGGL((moe_gemv_kernel<FMT, GU, RB, SLOT>), dim3(unsigned(grid)), dim3(kThreads),
+                     0, stream, a, tl.tiles, tl.n, L.tok, out);
   return hipGetLastError();
 }
 
 // Row blocks per wave: the largest of kMaxRB, ..., 2, 1 that still gives every resident
 // workgroup an item (the tile count is a device value; its host-side upper bound is used).
-template <int FMT, bool GU>
-hipError_t launch_stage(const GemvArgs& g, const MoeLaunch& L, void* out, int64_t n_out,
-                        hipStream_t stream) {
+template <int FMT, bool GU, bool SLOT>
+hipError_t launch_stage(const GemvArgs& g, const TileList& tl, const MoeLaunch& L, void* out,
+                        int64_t n_out, hipStream_t stream) {
   const int64_t wgs = int64_t(kWgPerCu) * cu_count();
   const int64_t per_block = GU ? 8 : 16;
   auto items = [&](int64_t rb) {
     const int64_t per_item = kWaves * rb * per_block;
-    return L.max_mtiles * ((n_out + per_item - 1) / per_item);
+    return tl.max_tiles * ((n_out + per_item - 1) / per_item);
   };
   if constexpr (kMaxRB >= 4) {
-    if (items(4) >= wgs) return launch_rb<FMT, GU, 4>(g, L, out, n_out, wgs, stream);
+    if (items(4) >= wgs) return launch_rb<FMT, GU, 4, SLOT>(g, tl, L, out, n_out, wgs, stream);
   }
-  if (items(2) >= wgs) return launch_rb<FMT, GU, 2>(g, L, out, n_out, wgs, stream);
-  return launch_rb<FMT, GU, 1>(g, L, out, n_out, wgs, stream);
+  if (items(2) >= wgs) return launch_rb<FMT, GU, 2, SLOT>(g, tl, L, out, n_out, wgs, stream);
+  return launch_rb<FMT, GU, 1, SLOT>(g, tl, L, out, n_out, wgs, stream);
 }
 
 }  // namespace
 
-template <int FMT>
-static hipError_t launch_gemv_fmt(const MoeLaunch& L, hipStream_t stream, int stage) {
+// SLOT: activations and h in the slot order of the NF4 MFMA-tile path (tail tiles of that
+// path); otherwise natural order.
+template <int FMT, bool SLOT>
+static hipError_t launch_gemv_fmt(const MoeLaunch& L, const TileList& tl, hipStream_t stream,
+                                  int stage) {
   GemvArgs g{};
   g.I = L.I;
   g.T = L.T;
@@ -451,18 +470,26 @@ static hipError_t launch_gemv_fmt(const MoeLaunch& L, hipStream_t stream, int st
     g.sc = L.s_gu;
     g.K = L.H;
     g.N = 2 * L.I;
-    return launch_stage<FMT, true>(g, L, L.h, L.I, stream);
+    return launch_stage<FMT, true, SLOT>(g, tl, L, L.h, L.I, stream);
   }
   g.a = L.h;
   g.wq = L.w_dn;
   g.sc = L.s_dn;
   g.K = L.I;
   g.N = L.H;
-  return launch_stage<FMT, false>(g, L, L.y, L.H, stream);
+  return launch_stage<FMT, false, SLOT>(g, tl, L, L.y, L.H, stream);
 }
 
 hipError_t launch_gemv(const MoeLaunch& L, hipStream_t stream, int stage) {
-  return L.fmt == 0 ? launch_gemv_fmt<0>(L, stream, stage) : launch_gemv_fmt<1>(L, stream, stage);
+  const TileList tl{L.tiles, L.n_mtiles, L.max_mtiles};
+  return L.fmt == 0 ? launch_gemv_fmt<0, false>(L, tl, stream, stage)
+                    : launch_gemv_fmt<1, false>(L, tl, stream, stage);
+}
+
+hipError_t launch_gemv_tails(const MoeLaunch& L, hipStream_t stream, int stage) {
+  const TileList tl{L.tiles + 4 * L.max_mtiles, L.n_mtiles + 1, L.max_stiles};
+  return L.fmt == 0 ? launch_gemv_fmt<0, true>(L, tl, stream, stage)
+                    : launch_gemv_fmt<1, false>(L, tl, stream, stage);
 }
 
 }  // namespace e4b

@@ -410,7 +410,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int32_t* wsum, int* t
 }
 
 // One workgroup: walk the experts in order and cut each expert's rows into bm-row tiles.  If
-// the last piece of an expert has at most `tail` rows (tail > 0), it is cut into 32-row
+// the last piece of an expert has at most `tail` rows (tail > 0), it is cut into 16-row
 // tiles instead, listed in tails[] (their count in n_mtiles[1]), so a full-size tile is not
 // spent on a few rows.
 __global__ void __launch_bounds__(256) build_tiles_kernel(const int32_t* __restrict__ offsets,
@@ -428,7 +428,7 @@ __global__ void __launch_bounds__(256) build_tiles_kernel(const int32_t* __restr
     const int nfull = cnt / bm, rem = cnt - nfull * bm;
     const bool split = rem > 0 && rem <= tail;
     const int nt = split ? nfull : (cnt + bm - 1) / bm;
-    const int ns = split ? (rem + 31) / 32 : 0;
+    const int ns = split ? (rem + kGemvTileRows - 1) / kGemvTileRows : 0;
     int tot, tot_s;
     const int first = run + block_exclusive_scan(nt, wsum, &tot);
     const int first_s = run_s + block_exclusive_scan(ns, wsum, &tot_s);
@@ -442,8 +442,8 @@ __global__ void __launch_bounds__(256) build_tiles_kernel(const int32_t* __restr
     for (int i = 0; i < ns; ++i) {
       int32_t* t = tails + 4 * int64_t(first_s + i);
       t[0] = e;
-      t[1] = start + nfull * bm + 32 * i;
-      t[2] = min(32, rem - 32 * i);
+      t[1] = start + nfull * bm + kGemvTileRows * i;
+      t[2] = min(kGemvTileRows, rem - kGemvTileRows * i);
       t[3] = 0;
     }
     run += tot;
@@ -491,9 +491,11 @@ static void record(const MoeLaunch& L, int i, hipStream_t stream) {
   if (L.events) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(L.events[i]), stream);
 }
 
-// One grouped GEMM stage over the main tiles, then over the 32-row tail tiles if any.
+// One grouped GEMM stage over the main tiles, then the streaming kernel over the 16-row tail
+// tiles if any (an expert's last few rows: streaming its weights once per 16 rows beats
+// running them as a mostly empty MFMA tile).
 template <int FMT, bool GU, int BM, int WAVES>
-static void launch_stage_tiles(const MoeLaunch& L, GemmArgs g, hipStream_t stream) {
+static hipError_t launch_stage_tiles(const MoeLaunch& L, GemmArgs g, hipStream_t stream) {
   const int64_t n_out = GU ? L.I : L.H;
   const int per_wave = GU ? 32 : 64;
   g.tiles = L.tiles;
@@ -501,13 +503,8 @@ static void launch_stage_tiles(const MoeLaunch& L, GemmArgs g, hipStream_t strea
   g.n_ntiles = int((n_out + WAVES * per_wave - 1) / (WAVES * per_wave));
   hipLaunchKernelGGL((moe_gemm_kernel<FMT, GU, BM, WAVES>),
                      dim3(unsigned(L.max_mtiles * g.n_ntiles)), dim3(WAVES * 64), 0, stream, g);
-  if (BM != 32 && L.max_stiles > 0) {
-    g.tiles = L.tiles + 4 * L.max_mtiles;
-    g.n_mtiles = L.n_mtiles + 1;
-    g.n_ntiles = int((n_out + per_wave - 1) / per_wave);
-    hipLaunchKernelGGL((moe_gemm_kernel<FMT, GU, 32, 1>),
-                       dim3(unsigned(L.max_stiles * g.n_ntiles)), dim3(64), 0, stream, g);
-  }
+  if (L.max_stiles > 0) return launch_gemv_tails(L, stream, GU ? 0 : 1);
+  return hipGetLastError();
 }
 
 template <int FMT, int BM, int WAVES>
@@ -524,7 +521,8 @@ static hipError_t launch_gemms(const MoeLaunch& L, hipStream_t stream) {
   g.out = L.h;
   g.K = L.H;
   g.N = 2 * L.I;
-  launch_stage_tiles<FMT, true, BM, WAVES>(L, g, stream);
+  hipError_t err = launch_stage_tiles<FMT, true, BM, WAVES>(L, g, stream);
+  if (err != hipSuccess) return err;
   record(L, 3, stream);
   // down + routing weight
   g.a = L.h;
@@ -533,8 +531,7 @@ static hipError_t launch_gemms(const MoeLaunch& L, hipStream_t stream) {
   g.out = L.y;
   g.K = L.I;
   g.N = L.H;
-  launch_stage_tiles<FMT, false, BM, WAVES>(L, g, stream);
-  return hipGetLastError();
+  return launch_stage_tiles<FMT, false, BM, WAVES>(L, g, stream);
 }
 
 template <int FMT>
