@@ -414,11 +414,13 @@ int cu_count() {
   return cached[dev];
 }
 
-// A list of 16-row tiles: the tile array, its device-side count and a host-side bound.
+// A list of 16-row tiles: the tile array, its device-side count, a host-side bound, and
+// whether these are the tail tiles of the MFMA-tile path.
 struct TileList {
   const int32_t* tiles;
   const int32_t* n;
   int64_t max_tiles;
+  bool tails;
 };
 
 template <int FMT, bool GU, int RB, bool SLOT>
@@ -441,6 +443,8 @@ template <int FMT, bool GU, bool SLOT>
 hipError_t launch_stage(const GemvArgs& g, const TileList& tl, const MoeLaunch& L, void* out,
                         int64_t n_out, hipStream_t stream) {
   const int64_t wgs = int64_t(kWgPerCu) * cu_count();
+  // tail tiles are few and their bound loose: one row block per wave gives the most items
+  if (tl.tails) return launch_rb<FMT, GU, 1, SLOT>(g, tl, L, out, n_out, wgs, stream);
   const int64_t per_block = GU ? 8 : 16;
   auto items = [&](int64_t rb) {
     const int64_t per_item = kWaves * rb * per_block;
@@ -481,13 +485,13 @@ static hipError_t launch_gemv_fmt(const MoeLaunch& L, const TileList& tl, hipStr
 }
 
 hipError_t launch_gemv(const MoeLaunch& L, hipStream_t stream, int stage) {
-  const TileList tl{L.tiles, L.n_mtiles, L.max_mtiles};
+  const TileList tl{L.tiles, L.n_mtiles, L.max_mtiles, false};
   return L.fmt == 0 ? launch_gemv_fmt<0, false>(L, tl, stream, stage)
                     : launch_gemv_fmt<1, false>(L, tl, stream, stage);
 }
 
 hipError_t launch_gemv_tails(const MoeLaunch& L, hipStream_t stream, int stage) {
-  const TileList tl{L.tiles + 4 * L.max_mtiles, L.n_mtiles + 1, L.max_stiles};
+  const TileList tl{L.tiles + 4 * L.max_mtiles, L.n_mtiles + 1, L.max_stiles, true};
   return L.fmt == 0 ? launch_gemv_fmt<0, true>(L, tl, stream, stage)
                     : launch_gemv_fmt<1, false>(L, tl, stream, stage);
 }
