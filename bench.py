@@ -17,6 +17,7 @@ bounded sample of the headline workload.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -127,6 +128,10 @@ def measure(torch, b: Batch, steps: int, warmup: int, flush_bytes: int = 0):
     torch.cuda.synchronize()
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
+    # no Python garbage collection inside the timed region (a collection that frees the
+    # previous layer's tensors there stalled the launch thread by milliseconds)
+    gc.collect()
+    gc.disable()
     wall0 = time.perf_counter()
     t_begin.record()
     for i in range(steps):
@@ -138,6 +143,7 @@ def measure(torch, b: Batch, steps: int, warmup: int, flush_bytes: int = 0):
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    gc.enable()
     stage_ms = np.array([[ev[i][j].elapsed_time(ev[i][j + 1]) for j in range(5)] for i in range(steps)])
     step_ms = np.array([a.elapsed_time(c) for a, c in step_ev])
     total_ms = t_begin.elapsed_time(t_end)
