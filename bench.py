@@ -303,7 +303,9 @@ def batch_report(torch, layer: Layer, T: int, steps: int, warmup: int, flush: in
     wl = b.wl
     n_active = b.active_experts()
     m = measure(torch, b, steps, warmup, flush)
-    rl = roofline(wl, n_active, m, None if flush else load_counters(wl.name))
+    # the counters were taken at each workload's own T; other batch sizes get none
+    same_T = wl.T == WORKLOADS[wl.name].T
+    rl = roofline(wl, n_active, m, load_counters(wl.name) if same_T and not flush else None)
     S = wl.T * wl.k
     ms = m["ms_per_step"]
     rep = {
