@@ -48,6 +48,21 @@ def assert_out_is_rne_of_f32(out_bf16: np.ndarray, out_f32: np.ndarray):
     assert np.array_equal(out_bf16, f32_to_bf16_bits(out_f32))
 
 
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bf16_violations(out_bf16: np.ndarray, ref: np.ndarray):
+    """The literal check of the bf16 output against the float64 reference, reported beside its
+    floor: (elements of out_bf16 outside the per-row bound, elements of the bf16 rounding of ref
+    itself outside it).  A bf16 half-ulp exceeds the bound for large |y|, so even a perfectly
+    computed output has violations (the floor); the gate proper is on the fp32 output."""
+    tau = omoe.tolerance(ref)[:, None]
+    got = bf16_bits_to_f64(out_bf16)
+    floor = bf16_bits_to_f64(f32_to_bf16_bits(ref.astype(np.float32)))
+    return int(np.sum(np.abs(got - ref) > tau)), int(np.sum(np.abs(floor - ref) > tau))
+
+
 class Layer:
     """Seeded inputs of one layer, on host (bits) and device; packed both ways."""
 

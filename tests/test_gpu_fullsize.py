@@ -4,7 +4,9 @@ Each full-size workload runs through the GPU path exactly as bench.py launches i
 packing, e4b_route_permute, e4b_moe_forward with the automatic path choice) and the sampled
 tokens' outputs are compared with float64 oracle outputs stored by
 tests/golden/make_expected.py (which calls only the oracle).  Properties checked on every
-row: the bf16 output is the round-to-nearest-even of the fp32 output.
+row: the bf16 output is the round-to-nearest-even of the fp32 output.  The literal bf16 check
+(bf16 output against the float64 oracle) is reported with its violation count beside the
+count for the bf16 rounding of the oracle itself, its floor.
 """
 import os
 
@@ -12,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import assert_out_is_rne_of_f32, assert_rows_within_tolerance, host
+from gpu_helpers import assert_out_is_rne_of_f32, assert_rows_within_tolerance, bf16_violations, host
 from moe_inputs import WORKLOADS, make_expert_weight, make_logits, make_x
 
 pytestmark = pytest.mark.gpu
@@ -51,7 +53,7 @@ def packed_layer(e4b, wl):
 
 
 @pytest.mark.parametrize("case,name,T", CASES, ids=[c[0] for c in CASES])
-def test_full_size_sampled_tokens(e4b, case, name, T):
+def test_full_size_sampled_tokens(e4b, case, name, T, record_property):
     path = os.path.join(GOLDEN, f"expected_{case}.npz")
     if not os.path.exists(path):
         pytest.fail(f"{path} missing: run tests/golden/make_expected.py")
@@ -73,3 +75,10 @@ def test_full_size_sampled_tokens(e4b, case, name, T):
     assert np.all(np.isfinite(o32))
     assert_rows_within_tolerance(o32[toks], exp["out"], case)
     assert_out_is_rne_of_f32(host(out), o32)
+    n_bad, n_floor = bf16_violations(host(out)[toks], exp["out"])
+    record_property("bf16_violations", n_bad)
+    record_property("bf16_floor", n_floor)
+    print(f"{case}: bf16 output outside the bound at {n_bad} of {exp['out'].size} sampled elements "
+          f"(bf16 rounding of the oracle itself: {n_floor})")
+    # an fp32 result within 1/20 of the bound can move a bf16 rounding by one ulp, not more
+    assert n_bad <= 3 * n_floor + 32
