@@ -7,9 +7,11 @@
 // gate_up / down stacks.
 //
 // Pipeline (all on the caller's stream, no device->host read-back):
-//   convert_x     x bf16 [T,H] -> fp16 (exact in fp16 range), k-slot order of the format
-//   build_tiles   per expert, ceil(rows/BM) row tiles of the expert-major slot order
+//   convert_x     x bf16 [T,H] -> fp16 (exact in fp16 range), k-slot order of the format;
+//                 its last workgroup also runs build_tiles: per expert, BM-row tiles of the
+//                 expert-major slot order, and 16-row tail tiles for a short last piece
 //   gemm<GU>      h[p, j] = silu(x_t . Wg[e,j]) * (x_t . Wu[e,j]) for the rows p of a tile
+//                 (tail tiles: the streaming kernel of gemv.hip, same operand order)
 //   gemm<DN>      y[p, n] = h[p] . Wd[e,n]   (sorted row p)
 //   combine       out[t] = sum_j topk_w[s] * y[inv[s]], s = t*k+j  (fixed order) -> fp32, bf16
 //                 (RNE); inv (slot -> sorted row) is written by convert_x
@@ -17,9 +19,10 @@
 // Tile structure of gemm: a workgroup owns BM rows of one expert and WAVES*64 weight rows
 // (GU: 32 gate + 32 matching up rows per wave, so SwiGLU is formed in registers).  Each
 // wave owns all BM rows x 64 weight rows and keeps its accumulators in registers
-// (v_mfma_f32_32x32x16_f16).  The activation tile (BM x 64 fp16) is staged through LDS,
-// double-buffered, and shared by the waves; each lane streams its own weight row's packed
-// bytes straight from HBM (16 bytes per 64-wide K step) and decodes them in registers.
+// (v_mfma_f32_32x32x16_f16).  The activation tile (BM x 64 fp16 per K step) comes through a
+// 4-stage LDS ring filled by direct buffer->LDS loads and is shared by the waves; each lane
+// streams its own weight rows' packed bytes straight from HBM (64 contiguous bytes per
+// 256-wide K group) and decodes them in registers.
 #include <type_traits>
 
 #include "e4b_device.h"
@@ -352,40 +355,6 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
 E4B_GEMM_INST_ALL(0)
 E4B_GEMM_INST_ALL(1)
 
-// x bf16 -> fp16 (exact for |x| in fp16's normal range), stored in the k-slot order of the
-// weight format inside each aligned group of 8.  Also inverts the routing permutation,
-// inv[slots[p]] = p for the S sorted rows p, and records each sorted row's token,
-// tok[p] = slots[p] / k.
-template <int FMT>
-__global__ void __launch_bounds__(256) convert_x_kernel(const uint16_t* __restrict__ x,
-                                                        _Float16* __restrict__ x16,
-                                                        int64_t n_chunks,
-                                                        const int32_t* __restrict__ slots,
-                                                        int64_t S, int32_t k,
-                                                        int32_t* __restrict__ inv,
-                                                        int32_t* __restrict__ tok) {
-  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
-  const int64_t n = n_chunks > S ? n_chunks : S;
-  for (int64_t q = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; q < n; q += stride) {
-    if (q < S) {
-      const int32_t sl = slots[q];
-      inv[sl] = int32_t(q);
-      tok[q] = sl / k;
-    }
-    if (q >= n_chunks) continue;
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(x + 8 * q);
-    _Float16 v[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = (_Float16)__uint_as_float(raw[i] << 16);
-      v[2 * i + 1] = (_Float16)__uint_as_float(raw[i] & 0xFFFF0000u);
-    }
-    f16x8 o;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[FMT == 0 ? nf4_elem_slot(i) : i] = v[i];
-    *reinterpret_cast<f16x8*>(x16 + 8 * q) = o;
-  }
-}
 
 // Exclusive prefix sum of v over the 256 threads of the workgroup; *total = the sum.
 __device__ __forceinline__ int block_exclusive_scan(int v, int32_t* wsum, int* total) {
@@ -409,15 +378,24 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int32_t* wsum, int* t
   return woff + incl - v;
 }
 
-// One workgroup: walk the experts in order and cut each expert's rows into bm-row tiles.  If
+// One workgroup walks the experts in order and cuts each expert's rows into bm-row tiles.  If
 // the last piece of an expert has at most `tail` rows (tail > 0), it is cut into 16-row
 // tiles instead, listed in tails[] (their count in n_mtiles[1]), so a full-size tile is not
 // spent on a few rows.
-__global__ void __launch_bounds__(256) build_tiles_kernel(const int32_t* __restrict__ offsets,
-                                                          int E, int bm, int tail,
-                                                          int32_t* __restrict__ tiles,
-                                                          int32_t* __restrict__ tails,
-                                                          int32_t* __restrict__ n_mtiles) {
+struct TileArgs {
+  const int32_t* offsets;
+  int E, bm, tail;
+  int32_t* tiles;
+  int32_t* tails;
+  int32_t* n_mtiles;
+};
+
+__device__ void build_tiles(const TileArgs& ta) {
+  const int32_t* __restrict__ offsets = ta.offsets;
+  const int E = ta.E, bm = ta.bm, tail = ta.tail;
+  int32_t* __restrict__ tiles = ta.tiles;
+  int32_t* __restrict__ tails = ta.tails;
+  int32_t* __restrict__ n_mtiles = ta.n_mtiles;
   __shared__ int32_t wsum[4];
   const int tid = threadIdx.x;
   int run = 0, run_s = 0;
@@ -452,6 +430,43 @@ __global__ void __launch_bounds__(256) build_tiles_kernel(const int32_t* __restr
   if (tid == 0) {
     n_mtiles[0] = run;
     n_mtiles[1] = run_s;
+  }
+}
+
+// x bf16 -> fp16 (exact for |x| in fp16's normal range), stored in the k-slot order of the
+// weight format inside each aligned group of 8.  Also inverts the routing permutation,
+// inv[slots[p]] = p for the S sorted rows p, and records each sorted row's token,
+// tok[p] = slots[p] / k.  The last workgroup first builds the tile list (build_tiles).
+template <int FMT>
+__global__ void __launch_bounds__(256) convert_x_kernel(const uint16_t* __restrict__ x,
+                                                        _Float16* __restrict__ x16,
+                                                        int64_t n_chunks,
+                                                        const int32_t* __restrict__ slots,
+                                                        int64_t S, int32_t k,
+                                                        int32_t* __restrict__ inv,
+                                                        int32_t* __restrict__ tok,
+                                                        TileArgs ta) {
+  if (blockIdx.x == gridDim.x - 1) build_tiles(ta);  // uniform over the workgroup
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  const int64_t n = n_chunks > S ? n_chunks : S;
+  for (int64_t q = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; q < n; q += stride) {
+    if (q < S) {
+      const int32_t sl = slots[q];
+      inv[sl] = int32_t(q);
+      tok[q] = sl / k;
+    }
+    if (q >= n_chunks) continue;
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(x + 8 * q);
+    _Float16 v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = (_Float16)__uint_as_float(raw[i] << 16);
+      v[2 * i + 1] = (_Float16)__uint_as_float(raw[i] & 0xFFFF0000u);
+    }
+    f16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[FMT == 0 ? nf4_elem_slot(i) : i] = v[i];
+    *reinterpret_cast<f16x8*>(x16 + 8 * q) = o;
   }
 }
 
@@ -540,15 +555,16 @@ static hipError_t launch_fmt(const MoeLaunch& L, hipStream_t stream) {
   // the streaming path takes activations in natural order for both formats
   const int64_t S = L.T * L.k, nchunks = L.T * L.H / 8;
   const unsigned gx = grid_1d(nchunks > S ? nchunks : S);
+  // one launch converts x and builds the tile list (the "build_tiles" stage stays empty)
+  const TileArgs ta{L.offsets, int(L.E), L.cfg.bm, L.tail_rows, L.tiles,
+                    L.tiles + 4 * L.max_mtiles, L.n_mtiles};
   if (FMT == 0 && !L.cfg.gemv)
     hipLaunchKernelGGL(convert_x_kernel<0>, dim3(gx), dim3(256), 0, stream, L.x, L.x16, nchunks,
-                       L.slots, S, L.k, L.inv, L.tok);
+                       L.slots, S, L.k, L.inv, L.tok, ta);
   else
     hipLaunchKernelGGL(convert_x_kernel<1>, dim3(gx), dim3(256), 0, stream, L.x, L.x16, nchunks,
-                       L.slots, S, L.k, L.inv, L.tok);
+                       L.slots, S, L.k, L.inv, L.tok, ta);
   record(L, 1, stream);
-  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, stream, L.offsets, int(L.E),
-                     L.cfg.bm, L.tail_rows, L.tiles, L.tiles + 4 * L.max_mtiles, L.n_mtiles);
   record(L, 2, stream);
   hipError_t err;
   if (L.cfg.gemv) {

@@ -2,7 +2,8 @@
 // and the expert-major, token-ordered slot permutation that groups every expert's rows
 // contiguously for the grouped GEMMs (grouped-nf4-gemm 0.25.0 project description, opening
 // section: one launch over all active experts, a router epilogue among the glue kernels).
-// The permutation is a stable counting sort over chunks of 1024 tokens:
+// The permutation is a stable counting sort over chunks of 1024 tokens (for at most 4096
+// slots, steps 2-4 are one launch, route_small_kernel):
 //
 //   1. topk_kernel     one wave per token: k rounds of a wave-wide arg-max under the order
 //                      (higher logit, then lower expert index); softmax weights
@@ -156,21 +157,14 @@ __global__ void __launch_bounds__(256) offsets_kernel(int32_t* __restrict__ cc, 
   if (tid == 255) offsets[E] = run;
 }
 
-// One workgroup per (chunk c, expert e): the chunk's tokens in order, with a ballot prefix
-// sum, so the slots of e land token-ascending from cc[c][e].
-__global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict__ ids, int64_t T,
-                                                      int E, int k,
-                                                      const int32_t* __restrict__ cc,
-                                                      int32_t* __restrict__ slots) {
-  __shared__ int32_t wave_tot[4];
-  const int e = int(blockIdx.x % unsigned(E));
-  const int64_t c = blockIdx.x / unsigned(E);
+// Slots of expert e among tokens [t_begin, t_end), in token order, written from slots[base]:
+// a ballot prefix sum per 256 tokens (stable, deterministic).  Whole workgroup.
+__device__ __forceinline__ void scatter_range(const int32_t* __restrict__ ids, int64_t t_begin,
+                                              int64_t t_end, int k, int e, int base,
+                                              int32_t* __restrict__ slots, int32_t* wave_tot) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int base = cc[c * E + e];
-  int64_t t_end = (c + 1) * kTokChunk;
-  if (t_end > T) t_end = T;
   int running = 0;
-  for (int64_t t0 = c * kTokChunk; t0 < t_end; t0 += 256) {
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += 256) {
     const int64_t t = t0 + tid;
     int flag = 0, jsel = 0;
     if (t < t_end) {
@@ -197,6 +191,57 @@ __global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict_
   }
 }
 
+// One workgroup per (chunk c, expert e): the chunk's tokens, from the first slot cc[c][e].
+__global__ void __launch_bounds__(256) scatter_kernel(const int32_t* __restrict__ ids, int64_t T,
+                                                      int E, int k,
+                                                      const int32_t* __restrict__ cc,
+                                                      int32_t* __restrict__ slots) {
+  __shared__ int32_t wave_tot[4];
+  const int e = int(blockIdx.x % unsigned(E));
+  const int64_t c = blockIdx.x / unsigned(E);
+  int64_t t_end = (c + 1) * kTokChunk;
+  if (t_end > T) t_end = T;
+  scatter_range(ids, c * kTokChunk, t_end, k, e, cc[c * E + e], slots, wave_tot);
+}
+
+// Few slots (T*k <= kSmallIds): one workgroup per expert counts the slots of lower experts
+// and its own directly from ids (every workgroup reads all ids, a few KB from L2), writes
+// its offset and scatters; one launch instead of the count / offsets / scatter passes.
+constexpr int64_t kSmallIds = 4096;
+
+__global__ void __launch_bounds__(256) route_small_kernel(const int32_t* __restrict__ ids,
+                                                          int64_t T, int E, int k,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ slots) {
+  __shared__ int32_t red[2][4];
+  __shared__ int32_t wave_tot[4];
+  const int e = int(blockIdx.x);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t n = T * k;
+  int below = 0, mine = 0;
+  for (int64_t i = tid; i < n; i += 256) {
+    const int v = ids[i];
+    below += v < e;
+    mine += v == e;
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    below += __shfl_xor(below, off);
+    mine += __shfl_xor(mine, off);
+  }
+  if (lane == 0) {
+    red[0][wave] = below;
+    red[1][wave] = mine;
+  }
+  __syncthreads();
+  const int base = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+  if (tid == 0) {
+    offsets[e] = base;
+    if (e == E - 1) offsets[E] = base + red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  }
+  scatter_range(ids, 0, T, k, e, base, slots, wave_tot);
+}
+
 hipError_t launch_route(const float* logits, int64_t T, int64_t E, int k, bool renorm,
                         int32_t* ids, float* w, int32_t* offsets, int32_t* slots, int32_t* cc,
                         hipStream_t stream) {
@@ -205,6 +250,11 @@ hipError_t launch_route(const float* logits, int64_t T, int64_t E, int k, bool r
     const int64_t blocks = (T + 3) / 4;
     hipLaunchKernelGGL(topk_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, logits, T,
                        int(E), k, renorm ? 1 : 0, ids, w);
+  }
+  if (T * k <= kSmallIds) {
+    hipLaunchKernelGGL(route_small_kernel, dim3(unsigned(E)), dim3(256), 0, stream, ids, T,
+                       int(E), k, offsets, slots);
+    return hipGetLastError();
   }
   hipLaunchKernelGGL(count_kernel, dim3(unsigned(chunks)), dim3(256), 0, stream, ids, T, int(E),
                      k, cc);
