@@ -5,8 +5,9 @@
 // The permutation is a stable counting sort over chunks of 1024 tokens (for at most 4096
 // slots, steps 2-4 are one launch, route_small_kernel):
 //
-//   1. topk_kernel     one wave per token: k rounds of a wave-wide arg-max under the order
-//                      (higher logit, then lower expert index); softmax weights
+//   1. topk_kernel     one wave per token: k rounds of a wave-wide arg-max (DPP lane moves)
+//                      under the order (higher logit, then lower expert index); softmax
+//                      weights
 //   2. count_kernel    one workgroup per chunk: LDS histogram of the chunk's picks, cc[c][e]
 //                      (no global atomics: per-pick atomics on a few hot counters serialised
 //                      badly, 80 us at T = 4096, E = 8)
@@ -28,6 +29,46 @@ __device__ __forceinline__ bool beats(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// One step of the wave-wide arg-max: combine (v, i) with the pair DPP control `ctrl` moves
+// in (lanes outside row_mask keep theirs).
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v),
+                                                              kCtrl, kRowMask, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(i, i, kCtrl, kRowMask, 0xF, false);
+  if (beats(ov, oi, v, i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+// Wave-wide arg-max under `beats`, with DPP lane moves (quad swaps, half-row and row
+// mirrors, then the row broadcasts of lanes 15 and 31), which lands the result in lane 63;
+// returned to every lane through a scalar read.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_step<0xB1, 0xF>(v, i);   // quad_perm [1,0,3,2]
+  argmax_step<0x4E, 0xF>(v, i);   // quad_perm [2,3,0,1]
+  argmax_step<0x141, 0xF>(v, i);  // row_half_mirror
+  argmax_step<0x140, 0xF>(v, i);  // row_mirror: every lane holds its row's result
+  argmax_step<0x142, 0xA>(v, i);  // row_bcast:15 into rows 1 and 3
+  argmax_step<0x143, 0xC>(v, i);  // row_bcast:31 into rows 2 and 3
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
+}
+
+// Wave-wide sum in a fixed order (same lane moves as wave_argmax), returned to every lane.
+__device__ __forceinline__ float wave_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xC, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+// PL = logits per lane (E <= 64 * PL), a compile-time bound so the per-lane scans are short.
+template <int PL>
 __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int64_t T,
                                                    int E, int k, int renorm,
                                                    int32_t* __restrict__ ids,
@@ -36,12 +77,11 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   const int64_t t = int64_t(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave exits together
   const float* row = logits + t * E;
-  float v[kMaxExpertsPerLane];
-  const int per_lane = (E + 63) / 64;
+  float v[PL];
 #pragma unroll
-  for (int i = 0; i < kMaxExpertsPerLane; ++i) {
+  for (int i = 0; i < PL; ++i) {
     const int e = lane + 64 * i;
-    v[i] = (i < per_lane && e < E) ? row[e] : -INFINITY;
+    v[i] = (e < E) ? row[e] : -INFINITY;
   }
   uint32_t taken = 0;  // bit i: my entry i already chosen
   int my_id = 0;
@@ -50,22 +90,14 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
 #pragma unroll
-    for (int i = 0; i < kMaxExpertsPerLane; ++i) {
+    for (int i = 0; i < PL; ++i) {
       const int e = lane + 64 * i;
-      if (i < per_lane && e < E && !((taken >> i) & 1u) && beats(v[i], e, bv, bi)) {
+      if (e < E && !((taken >> i) & 1u) && beats(v[i], e, bv, bi)) {
         bv = v[i];
         bi = e;
       }
     }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (beats(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    wave_argmax(bv, bi);
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     if (lane == j) {
       my_id = bi;
@@ -80,13 +112,12 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
   } else {
     denom = 0.f;
 #pragma unroll
-    for (int i = 0; i < kMaxExpertsPerLane; ++i) {
+    for (int i = 0; i < PL; ++i) {
       const int e = lane + 64 * i;
-      if (i < per_lane && e < E) denom += expf(v[i] - vmax);
+      if (e < E) denom += expf(v[i] - vmax);
     }
   }
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) denom += __shfl_xor(denom, off);
+  denom = wave_sum(denom);
   if (lane < k) {
     ids[t * k + lane] = my_id;
     wts[t * k + lane] = ex / denom;
@@ -248,8 +279,17 @@ hipError_t launch_route(const float* logits, int64_t T, int64_t E, int k, bool r
   const int chunks = route_chunks(T);
   if (T > 0) {
     const int64_t blocks = (T + 3) / 4;
-    hipLaunchKernelGGL(topk_kernel, dim3(unsigned(blocks)), dim3(256), 0, stream, logits, T,
-                       int(E), k, renorm ? 1 : 0, ids, w);
+    const unsigned g = unsigned(blocks);
+    const int rn = renorm ? 1 : 0;
+    if (E <= 64)
+      hipLaunchKernelGGL(topk_kernel<1>, dim3(g), dim3(256), 0, stream, logits, T, int(E), k, rn, ids, w);
+    else if (E <= 128)
+      hipLaunchKernelGGL(topk_kernel<2>, dim3(g), dim3(256), 0, stream, logits, T, int(E), k, rn, ids, w);
+    else if (E <= 256)
+      hipLaunchKernelGGL(topk_kernel<4>, dim3(g), dim3(256), 0, stream, logits, T, int(E), k, rn, ids, w);
+    else
+      hipLaunchKernelGGL(topk_kernel<kMaxExpertsPerLane>, dim3(g), dim3(256), 0, stream, logits, T,
+                         int(E), k, rn, ids, w);
   }
   if (T * k <= kSmallIds) {
     hipLaunchKernelGGL(route_small_kernel, dim3(unsigned(E)), dim3(256), 0, stream, ids, T,
