@@ -3,6 +3,8 @@
 // no alternative code path: on a device other than gfx950 every compute entry point fails.
 #include <string.h>
 
+#include <atomic>
+
 #include "e4b.h"
 #include "e4b_internal.h"
 
@@ -16,18 +18,19 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // 1 = gfx950, -1 = other arch, 0 = not yet probed.
-int g_arch_ok[kMaxDevices];
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other (idempotent)
 
 int check_device() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return E4B_ERR_HIP;
   if (dev < 0 || dev >= kMaxDevices) return E4B_ERR_UNSUPPORTED;
-  if (g_arch_ok[dev] == 0) {
+  if (g_arch_ok[dev].load(std::memory_order_relaxed) == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return E4B_ERR_HIP;
-    g_arch_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_arch_ok[dev].store(strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1,
+                         std::memory_order_relaxed);
   }
-  return g_arch_ok[dev] == 1 ? E4B_OK : E4B_ERR_UNSUPPORTED;
+  return g_arch_ok[dev].load(std::memory_order_relaxed) == 1 ? E4B_OK : E4B_ERR_UNSUPPORTED;
 }
 
 int launched(hipError_t e) { return e == hipSuccess ? E4B_OK : E4B_ERR_HIP; }

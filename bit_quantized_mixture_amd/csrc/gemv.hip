@@ -30,6 +30,8 @@
 // MFMA (i, q) takes dword q of load i: K = 64*g + 32*i + 8*q + [0, 8) inside the step; the
 // activation chunk with the same K is read from LDS for token r.  Activations and h are in
 // natural K order on this path (the table yields the two elements of a byte in order).
+#include <atomic>
+
 #include "e4b_device.h"
 #include "e4b_internal.h"
 
@@ -401,17 +403,17 @@ __global__ void __launch_bounds__(kThreads)
 }
 
 int cu_count() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];  // 0 = not read yet; the value read is idempotent
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // A list of 16-row tiles: the tile array, its device-side count, a host-side bound, and
