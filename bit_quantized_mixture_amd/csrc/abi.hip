@@ -18,7 +18,7 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // 1 = gfx950, -1 = other arch, 0 = not yet probed.
-std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other (idempotent)
+std::atomic<int> g_arch_ok[kMaxDevices];
 
 int check_device() {
   int dev = 0;
