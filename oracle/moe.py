@@ -17,6 +17,13 @@ Readings where the pages are silent:
 * The first I rows of gate_up are the gate, the next I rows the up projection.
 * h = silu(G) * U with silu(g) = g / (1 + exp(-g)); Y = h W_down^T; out[t] = sum over the
   token's k slots of weight * Y.
+
+Expert variant of the MXFP4 family (experts4bit-qlora 0.35.0 project description, Scope:
+MXFP4 experts with per-expert biases and a clamped GLU; the pages give no formula, so the
+plainest reading is the released model family's own definition): gate and up rows interleaved (row
+2j gate j, row 2j+1 up j), a bias on each gate_up row and on each down row, and
+h = min(G, L) * sigmoid(a * min(G, L)) * (clip(U, -L, L) + 1) with L = 7 and a = 1.702
+(g * sigmoid(1.702 g) is the sigmoid approximation of the Gaussian-error gate g * Phi(g)).
 """
 from __future__ import annotations
 
@@ -43,20 +50,47 @@ def silu(g: np.ndarray) -> np.ndarray:
         return g / (1.0 + np.exp(-g))
 
 
-def expert_mlp(x: np.ndarray, w_gu: np.ndarray, w_dn: np.ndarray) -> np.ndarray:
-    """SwiGLU expert MLP in float64: x [M, H], w_gu [2I, H], w_dn [H, I] -> [M, H]."""
+GLU_LIMIT = 7.0
+GLU_ALPHA = 1.702
+
+
+def clamped_glu(g: np.ndarray, u: np.ndarray, alpha: float = GLU_ALPHA,
+                limit: float = GLU_LIMIT) -> np.ndarray:
+    """min(g, limit) * sigmoid(alpha * min(g, limit)) * (clip(u, -limit, limit) + 1)."""
+    gc = np.minimum(g, limit)
+    uc = np.clip(u, -limit, limit)
+    with np.errstate(over="ignore"):
+        return gc / (1.0 + np.exp(-alpha * gc)) * (uc + 1.0)
+
+
+def expert_mlp(x: np.ndarray, w_gu: np.ndarray, w_dn: np.ndarray, act: str = "swiglu",
+               interleaved: bool = False, b_gu=None, b_dn=None) -> np.ndarray:
+    """Expert MLP in float64: x [M, H], w_gu [2I, H], w_dn [H, I] -> [M, H].
+
+    act "swiglu": silu(G) * U; "clamped_glu": clamped_glu(G, U).  Gate / up rows are the two
+    halves of w_gu, or interleaved (even rows gate, odd rows up).  b_gu [2I] (same row order
+    as w_gu) and b_dn [H] are added to the products when given.
+    """
     I = w_dn.shape[1]
-    g = x @ w_gu[:I].T
-    u = x @ w_gu[I:].T
-    return (silu(g) * u) @ w_dn.T
+    gu = x @ w_gu.T
+    if b_gu is not None:
+        gu = gu + np.asarray(b_gu, np.float64)
+    g, u = (gu[:, 0::2], gu[:, 1::2]) if interleaved else (gu[:, :I], gu[:, I:])
+    h = silu(g) * u if act == "swiglu" else clamped_glu(g, u)
+    y = h @ w_dn.T
+    if b_dn is not None:
+        y = y + np.asarray(b_dn, np.float64)
+    return y
 
 
 def forward(fmt: str, x_bits: np.ndarray, gu_packed, gu_scales, dn_packed, dn_scales,
-            ids: np.ndarray, weights: np.ndarray, tokens=None) -> np.ndarray:
+            ids: np.ndarray, weights: np.ndarray, tokens=None, act: str = "swiglu",
+            interleaved: bool = False, b_gu=None, b_dn=None) -> np.ndarray:
     """out [len(tokens), H] float64 for the selected tokens (all tokens by default).
 
     Experts are visited one at a time; each expert's slice of the packed stacks is
-    decoded and applied to the tokens (among the selected ones) routed to it.
+    decoded and applied to the tokens (among the selected ones) routed to it.  act,
+    interleaved, b_gu [E, 2I] and b_dn [E, H] select the expert variant (expert_mlp).
     """
     T, k = ids.shape
     tokens = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
@@ -69,7 +103,9 @@ def forward(fmt: str, x_bits: np.ndarray, gu_packed, gu_scales, dn_packed, dn_sc
         rows, js = np.nonzero(sub_ids == e)
         w_gu = decode_expert(fmt, gu_packed, gu_scales, int(e))
         w_dn = decode_expert(fmt, dn_packed, dn_scales, int(e))
-        y = expert_mlp(x[rows], w_gu, w_dn)
+        y = expert_mlp(x[rows], w_gu, w_dn, act, interleaved,
+                       None if b_gu is None else np.asarray(b_gu)[int(e)],
+                       None if b_dn is None else np.asarray(b_dn)[int(e)])
         out[rows] += sub_w[rows, js][:, None] * y
     return out
 

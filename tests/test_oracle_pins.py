@@ -399,3 +399,104 @@ def test_forward_zero_input_and_weight_linearity():
 def test_tolerance_formula():
     ref = np.array([[3.0, 4.0, 0.0, 0.0]])
     assert np.allclose(moe.tolerance(ref), 8e-3 * 5.0 / 2.0 + 1e-3)
+
+
+# ------------------------------------------------------ clamped-GLU / interleaved variant
+
+def test_clamped_glu_gate_is_the_sigmoid_approximation_of_the_gaussian_gate():
+    """sigmoid(1.702 g) is the well-known logistic approximation of the normal CDF Phi(g):
+    a = 1.702 is about where the worst gap over the real line is smallest, just under 0.01
+    (the gate factor is recovered as clamped_glu(g, 0) / g, below the clamp)."""
+    g = np.linspace(-6.0, 6.0, 2000)                    # even count: g = 0 is not sampled
+    phi = 0.5 * (1.0 + np.array([math.erf(v / math.sqrt(2.0)) for v in g]))
+    gap = lambda a: np.max(np.abs(moe.clamped_glu(g, np.zeros_like(g), alpha=a) / g - phi))
+    assert gap(moe.GLU_ALPHA) < 0.0095
+    assert gap(moe.GLU_ALPHA) < gap(1.68) and gap(moe.GLU_ALPHA) < gap(1.72)
+    assert gap(1.0) > 0.05
+
+
+def test_clamped_glu_limits():
+    """Gate clamped from above only, up clamped on both sides, at 7."""
+    big = np.array([7.0, 8.0, 1e6])
+    up = np.array([0.5])
+    assert np.all(moe.clamped_glu(big, up) == moe.clamped_glu(np.array([7.0]), up))
+    g = np.array([2.0])
+    assert moe.clamped_glu(g, np.array([1e9])) == moe.clamped_glu(g, np.array([7.0]))
+    assert moe.clamped_glu(g, np.array([-1e9])) == moe.clamped_glu(g, np.array([-7.0]))
+    assert moe.clamped_glu(g, np.array([-1.0])) == 0.0      # (up + 1) = 0
+    # a very negative gate is not clamped: the output vanishes like g * exp(a g)
+    assert abs(moe.clamped_glu(np.array([-40.0]), np.array([3.0]))[0]) < 1e-25
+    # large a turns the gate into relu(min(g, 7))
+    gg = np.array([-3.0, -0.5, 0.25, 5.0, 9.0])
+    assert np.allclose(moe.clamped_glu(gg, np.zeros(5), alpha=1e4), np.minimum(np.maximum(gg, 0), 7.0))
+
+
+def _variant_problem(fmt="mxfp4", E=3, H=64, I=64, T=6, k=2, seed=5):
+    x, gp, gs, dp, ds, ids, w = _tiny_problem(fmt, E, H, I, T, k, seed)
+    rng = np.random.default_rng(seed + 1)
+    b_gu = rng.standard_normal((E, 2 * I)) * 0.5
+    b_dn = rng.standard_normal((E, H)) * 0.5
+    return x, gp, gs, dp, ds, ids, w, b_gu, b_dn
+
+
+def test_variant_matches_pure_python_loops():
+    E, H, I, T, k = 3, 64, 64, 6, 2
+    x, gp, gs, dp, ds, ids, w, b_gu, b_dn = _variant_problem(E=E, H=H, I=I, T=T, k=k)
+    out = moe.forward("mxfp4", x, gp, gs, dp, ds, ids, w, act="clamped_glu", interleaved=True,
+                      b_gu=b_gu, b_dn=b_dn)
+    xf = moe.bf16_bits_to_f64(x).tolist()
+    ref = [[0.0] * H for _ in range(T)]
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            Wg = moe.decode_expert("mxfp4", gp, gs, e).tolist()
+            Wd = moe.decode_expert("mxfp4", dp, ds, e).tolist()
+            h = []
+            for i in range(I):
+                g = sum(xf[t][c] * Wg[2 * i][c] for c in range(H)) + b_gu[e][2 * i]
+                u = sum(xf[t][c] * Wg[2 * i + 1][c] for c in range(H)) + b_gu[e][2 * i + 1]
+                g = min(g, 7.0)
+                u = max(-7.0, min(u, 7.0))
+                h.append(g / (1.0 + math.exp(-1.702 * g)) * (u + 1.0))
+            for n in range(H):
+                y = sum(h[i] * Wd[n][i] for i in range(I)) + b_dn[e][n]
+                ref[t][n] += float(w[t, j]) * y
+    ref = np.array(ref)
+    assert np.max(np.abs(out - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def test_variant_layouts_agree_after_row_permutation():
+    """Interleaved gate/up rows give the same layer as the halves layout of the same rows."""
+    from moe_inputs import f32_to_bf16_bits
+    E, H, I, T, k = 2, 64, 64, 5, 2
+    rng = np.random.default_rng(9)
+    x = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    w_half = f32_to_bf16_bits((0.1 * rng.standard_normal((E, 2 * I, H))).astype(np.float32))
+    perm = np.empty(2 * I, np.int64)
+    perm[0::2] = np.arange(I)
+    perm[1::2] = I + np.arange(I)
+    w_inter = w_half[:, perm]                      # row 2j = gate j, row 2j+1 = up j
+    b_half = rng.standard_normal((E, 2 * I))
+    wdn = f32_to_bf16_bits((0.1 * rng.standard_normal((E, H, I))).astype(np.float32))
+    gp1, gs1 = nf4.quantize_pack(w_half)
+    gp2, gs2 = nf4.quantize_pack(w_inter)
+    dp, ds = nf4.quantize_pack(wdn)
+    ids, w, *_ = route.route(rng.standard_normal((T, E)).astype(np.float32), k)
+    for act in ("swiglu", "clamped_glu"):
+        a = moe.forward("nf4", x, gp1, gs1, dp, ds, ids, w, act=act, b_gu=b_half)
+        b = moe.forward("nf4", x, gp2, gs2, dp, ds, ids, w, act=act, interleaved=True,
+                        b_gu=b_half[:, perm])
+        assert np.allclose(a, b, rtol=1e-13, atol=1e-15)
+
+
+def test_variant_biases_alone():
+    """Zero weights: every expert's output is its down bias, and the layer is the routing
+    weighted sum of those biases."""
+    E, H, I, T, k = 4, 64, 64, 7, 3
+    x, gp, gs, dp, ds, ids, w, b_gu, b_dn = _variant_problem("nf4", E=E, H=H, I=I, T=T, k=k)
+    zero_gu = nf4.quantize_pack(np.zeros((E, 2 * I, H), np.uint16))
+    zero_dn = nf4.quantize_pack(np.zeros((E, H, I), np.uint16))
+    out = moe.forward("nf4", x, *zero_gu, *zero_dn, ids, w, act="clamped_glu", interleaved=True,
+                      b_gu=b_gu, b_dn=b_dn)
+    ref = np.einsum("tj,tjh->th", w.astype(np.float64), b_dn[ids])
+    assert np.allclose(out, ref, rtol=1e-14, atol=1e-15)
