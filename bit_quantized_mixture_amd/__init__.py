@@ -14,7 +14,7 @@ import torch
 
 __all__ = [
     "E4BError", "E4B_FMT_NF4", "E4B_FMT_MXFP4", "E4B_PATH_AUTO", "E4B_PATH_GEMM", "E4B_PATH_GEMV",
-    "E4B_ROUTE_RENORMALIZE", "lib_path", "e4b_version", "e4b_status_string", "e4b_pack_nf4",
+    "E4B_ROUTE_RENORMALIZE", "E4B_ACT_CLAMPED_GLU", "E4B_GU_INTERLEAVED", "lib_path", "e4b_version", "e4b_status_string", "e4b_pack_nf4",
     "e4b_pack_mxfp4", "e4b_route_workspace_bytes", "e4b_route_permute", "e4b_moe_workspace_bytes",
     "e4b_moe_forward", "MoeArgs",
 ]
@@ -23,6 +23,7 @@ E4B_FMT_NF4, E4B_FMT_MXFP4 = 0, 1
 E4B_PATH_AUTO, E4B_PATH_GEMM, E4B_PATH_GEMV = 0, 1, 2
 E4B_TILE_AUTO, E4B_TILE_32, E4B_TILE_128, E4B_TILE_256 = 0x0, 0x4, 0x8, 0xC
 E4B_ROUTE_RENORMALIZE = 1
+E4B_ACT_CLAMPED_GLU, E4B_GU_INTERLEAVED = 0x10, 0x20
 _FMT = {"nf4": E4B_FMT_NF4, "mxfp4": E4B_FMT_MXFP4, E4B_FMT_NF4: E4B_FMT_NF4, E4B_FMT_MXFP4: E4B_FMT_MXFP4}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,6 +45,7 @@ class MoeArgs(ctypes.Structure):
         ("topk_w", _vp), ("expert_offsets", _vp), ("sorted_slots", _vp),
         ("out", _vp), ("out_f32", _vp), ("ws", _vp), ("ws_bytes", _sz),
         ("flags", _i32), ("reserved", _i32), ("stage_events", ctypes.POINTER(_vp)),
+        ("b_gu", _vp), ("b_dn", _vp),
     ]
 
 
@@ -193,10 +195,13 @@ def e4b_moe_workspace_bytes(fmt, E: int, H: int, I: int, T: int, k: int, path: i
 
 def e4b_moe_forward(fmt, x, w_gu, s_gu, w_dn, s_dn, topk_w, expert_offsets, sorted_slots, k: int,
                     out=None, out_f32=None, ws=None, path: int = E4B_PATH_AUTO, stream=None,
-                    stage_events=None):
+                    stage_events=None, act: str = "swiglu", interleaved: bool = False,
+                    b_gu=None, b_dn=None):
     """MoE expert layer on packed weights.  Returns (out bf16 [T, H], out_f32 or None).
 
     `out_f32`: pass True to allocate the float32 output, a tensor to fill it, None to skip.
+    `act` "swiglu" or "clamped_glu", `interleaved` gate/up row order, `b_gu` [E, 2I] and
+    `b_dn` [E, H] float32 biases (or None): the expert variant flags of include/e4b.h.
     `stage_events`: None, or 6 torch.cuda.Event (enable_timing=True), each recorded once
     beforehand so that it exists; the call records them around its 5 stages.
     """
@@ -212,8 +217,16 @@ def e4b_moe_forward(fmt, x, w_gu, s_gu, w_dn, s_dn, topk_w, expert_offsets, sort
     if ws is None:
         need = e4b_moe_workspace_bytes(fmt, E, H, I, T, k, path)
         ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    if act not in ("swiglu", "clamped_glu"):
+        raise ValueError(f"act must be 'swiglu' or 'clamped_glu', not {act!r}")
+    flags = path | (E4B_ACT_CLAMPED_GLU if act == "clamped_glu" else 0) | (E4B_GU_INTERLEAVED if interleaved else 0)
+    for name, b, n in (("b_gu", b_gu, (E, 2 * I)), ("b_dn", b_dn, (E, H))):
+        if b is not None:
+            _need(b, name, (torch.float32,), n)
     a = _moe_args(fmt, x, w_gu, s_gu, w_dn, s_dn, topk_w, expert_offsets, sorted_slots, E, H, I, k,
-                  out, out_f32, ws, path)
+                  out, out_f32, ws, flags)
+    a.b_gu = None if b_gu is None else b_gu.data_ptr()
+    a.b_dn = None if b_dn is None else b_dn.data_ptr()
     if stage_events is not None:
         if len(stage_events) != 6:
             raise ValueError("stage_events needs 6 events")

@@ -107,7 +107,8 @@ int check_forward_shape(const e4b_moe_args* a) {
   if (a->fmt != E4B_FMT_NF4 && a->fmt != E4B_FMT_MXFP4) return E4B_ERR_ARG;
   if (a->E <= 0 || a->H <= 0 || a->I <= 0 || a->T < 0 || a->k < 1) return E4B_ERR_ARG;
   if (a->k > a->E) return E4B_ERR_ARG;
-  if ((a->flags & ~(E4B_PATH_MASK | E4B_TILE_MASK)) != 0 || (a->flags & E4B_PATH_MASK) == 3)
+  if ((a->flags & ~(E4B_PATH_MASK | E4B_TILE_MASK | E4B_ACT_CLAMPED_GLU | E4B_GU_INTERLEAVED)) != 0 ||
+      (a->flags & E4B_PATH_MASK) == 3)
     return E4B_ERR_ARG;
   // a row-tile override names an MFMA tile; it cannot go with the streaming path
   if ((a->flags & E4B_PATH_MASK) == E4B_PATH_GEMV && (a->flags & E4B_TILE_MASK) != 0)
@@ -127,7 +128,7 @@ int check_forward_shape(const e4b_moe_args* a) {
 
 extern "C" {
 
-int e4b_version(void) { return 100; }
+int e4b_version(void) { return 200; }
 
 const char* e4b_status_string(int status) {
   switch (status) {
@@ -206,7 +207,8 @@ int e4b_moe_forward(const e4b_moe_args* a, void* stream) {
       !a->expert_offsets || !a->sorted_slots || !a->out || !a->ws)
     return E4B_ERR_ARG;
   const void* ptrs[] = {a->x, a->w_gu, a->s_gu, a->w_dn, a->s_dn, a->topk_w,
-                        a->expert_offsets, a->sorted_slots, a->out, a->out_f32, a->ws};
+                        a->expert_offsets, a->sorted_slots, a->out, a->out_f32, a->ws,
+                        a->b_gu, a->b_dn};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return E4B_ERR_ALIGN;
   FwdLayout L;
@@ -238,6 +240,10 @@ int e4b_moe_forward(const e4b_moe_args* a, void* stream) {
   M.slots = a->sorted_slots;
   M.out = a->out;
   M.out_f32 = a->out_f32;
+  M.b_gu = a->b_gu;
+  M.b_dn = a->b_dn;
+  M.clamped_glu = (a->flags & E4B_ACT_CLAMPED_GLU) ? 1 : 0;
+  M.interleaved = (a->flags & E4B_GU_INTERLEAVED) ? 1 : 0;
   M.x16 = reinterpret_cast<_Float16*>(ws + L.off_x16);
   M.h = reinterpret_cast<_Float16*>(ws + L.off_h);
   M.y = reinterpret_cast<float*>(ws + L.off_y);

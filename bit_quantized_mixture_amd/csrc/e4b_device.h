@@ -183,6 +183,14 @@ __device__ __forceinline__ float swiglu(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
+// Clamped GLU of the MXFP4 family's expert variant: the gate clamped from above at 7, the up
+// input to [-7, 7], gate * sigmoid(1.702 * gate) * (up + 1).
+__device__ __forceinline__ float clamped_glu(float g, float u) {
+  const float gc = fminf(g, 7.0f);
+  const float uc = fminf(fmaxf(u, -7.0f), 7.0f);
+  return gc * __builtin_amdgcn_rcpf(1.0f + __expf(-1.702f * gc)) * (uc + 1.0f);
+}
+
 // float32 -> bfloat16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

@@ -48,6 +48,10 @@ struct MoeLaunch {
   const int32_t* slots;
   uint16_t* out;
   float* out_f32;
+  const float* b_gu;  // nullable [E, 2I]
+  const float* b_dn;  // nullable [E, H]
+  int clamped_glu;    // activation: 0 silu(G) * U, 1 clamped GLU
+  int interleaved;    // gate_up rows: 0 halves, 1 interleaved
   // workspace carve-outs
   _Float16* x16;   // [T, H]
   _Float16* h;     // [S, I]

@@ -68,6 +68,9 @@ struct GemvArgs {
   int64_t I;
   int64_t T, S;            // tokens, routed rows (rows of x16 and of h)
   int32_t n_rblocks;       // weight-row blocks per expert
+  int32_t clamped_glu;     // gate_up activation: 0 silu(G) * U, 1 clamped GLU
+  int32_t interleaved;     // gate_up rows: 0 halves (gate j, up I + j), 1 interleaved
+  const float* bias;       // nullable [E, N], added to the products
 };
 
 // Index arrays read with uniform addresses inside the persistent loop are separate
@@ -133,6 +136,7 @@ __device__ __forceinline__ int32_t lane_row(const GemvArgs& p, int rb, int wave,
     const int32_t I = int32_t(p.I);
     int32_t j = rb * (kWaves * RB * 8) + (wave * RB + b) * 8 + (r & 7);
     j = j < I ? j : I - 1;
+    if (p.interleaved) return r < 8 ? 2 * j : 2 * j + 1;
     return r < 8 ? j : I + j;
   }
   const int32_t N = int32_t(p.N);
@@ -304,14 +308,28 @@ __device__ __forceinline__ void store_block(const GemvArgs& p, const Ptrs& pt,
     if (g < 2 && r < st.rows) {
       _Float16* h = reinterpret_cast<_Float16*>(pt.out) + int64_t(st.row0 + r) * p.I;
       const int32_t j0 = st.rb * (kWaves * RB * 8) + (wave * RB + b) * 8 + 4 * g;
+      const float* bias = p.bias ? p.bias + int64_t(st.e) * p.N : nullptr;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (j0 + i < int32_t(p.I)) h[act_pos<SLOT ? 0 : 1>(j0 + i)] = (_Float16)swiglu(acc[i], up[i]);
+      for (int i = 0; i < 4; ++i) {
+        const int32_t j = j0 + i;
+        if (j < int32_t(p.I)) {
+          float gv = acc[i], uv = up[i];
+          if (bias) {
+            gv += bias[p.interleaved ? 2 * j : j];
+            uv += bias[p.interleaved ? 2 * j + 1 : int32_t(p.I) + j];
+          }
+          h[act_pos<SLOT ? 0 : 1>(j)] = (_Float16)(p.clamped_glu ? clamped_glu(gv, uv) : swiglu(gv, uv));
+        }
+      }
     }
   } else if (r < st.rows) {
     float* y = reinterpret_cast<float*>(pt.out) + int64_t(st.row0 + r) * p.N;
     const int32_t n0 = st.rb * (kWaves * RB * 16) + (wave * RB + b) * 16 + 4 * g;
-    if (n0 < int32_t(p.N)) *reinterpret_cast<f32x4*>(y + n0) = acc;  // N % 64 == 0
+    if (n0 < int32_t(p.N)) {  // N % 64 == 0
+      f32x4 v = acc;
+      if (p.bias) v += *reinterpret_cast<const f32x4*>(p.bias + int64_t(st.e) * p.N + n0);
+      *reinterpret_cast<f32x4*>(y + n0) = v;
+    }
   }
 }
 
@@ -470,6 +488,9 @@ static hipError_t launch_gemv_fmt(const MoeLaunch& L, const TileList& tl, hipStr
   g.I = L.I;
   g.T = L.T;
   g.S = L.T * L.k;
+  g.clamped_glu = L.clamped_glu;
+  g.interleaved = L.interleaved;
+  g.bias = stage == 0 ? L.b_gu : L.b_dn;
   if (stage == 0) {
     g.a = L.x16;
     g.wq = L.w_gu;

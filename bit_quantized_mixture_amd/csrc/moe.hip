@@ -53,6 +53,9 @@ struct GemmArgs {
   int64_t T;               // tokens (rows of x16; h has T * k_top rows)
   int32_t k_top;
   int32_t n_ntiles;
+  const float* bias;       // nullable [E, N]: added to the products (GU before the activation)
+  int32_t clamped_glu;     // GU activation: 0 silu(G) * U, 1 clamped GLU
+  int32_t interleaved;     // GU rows: 0 halves (gate j, up I + j), 1 interleaved (2j, 2j + 1)
 };
 
 
@@ -76,8 +79,8 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
     const int64_t j = int64_t(nt) * (WAVES * 32) + wave * 32 + col;
     nvalid[0] = nvalid[1] = j < p.I;
     const int64_t jc = j < p.I ? j : p.I - 1;
-    nrow[0] = jc;
-    nrow[1] = p.I + jc;
+    nrow[0] = p.interleaved ? 2 * jc : jc;
+    nrow[1] = p.interleaved ? 2 * jc + 1 : p.I + jc;
   } else {
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
@@ -308,36 +311,72 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
   // ---- epilogue.  Accumulator element r of a 32x32 block: row 8*(r/4) + 4*half + r%4,
-  // column = col.
+  // column = col.  The plain SwiGLU / unbiased forms are kept as their own branches: the
+  // stores then take their data straight from the accumulators.
   if (GU) {
     if (!nvalid[0]) return;
     const int64_t j = int64_t(nt) * (WAVES * 32) + wave * 32 + col;
     _Float16* hout = reinterpret_cast<_Float16*>(p.out);
     const int64_t pos = act_pos<FMT>(j);
+    if (!p.bias && !p.clamped_glu) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+      for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (row < rows) {
-          const float g = acc[rb][0][r];
-          const float u = acc[rb][1][r];
-          const float hv = g / (1.0f + __expf(-g)) * u;
-          hout[int64_t(row0 + row) * p.I + pos] = (_Float16)hv;
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (row < rows) {
+            const float g = acc[rb][0][r];
+            const float u = acc[rb][1][r];
+            hout[int64_t(row0 + row) * p.I + pos] = (_Float16)(g / (1.0f + __expf(-g)) * u);
+          }
+        }
+      }
+    } else {
+      const float bg = p.bias ? p.bias[int64_t(e) * p.N + nrow[0]] : 0.0f;
+      const float bu = p.bias ? p.bias[int64_t(e) * p.N + nrow[1]] : 0.0f;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (row < rows) {
+            const float g = acc[rb][0][r] + bg;
+            const float u = acc[rb][1][r] + bu;
+            const float hv = p.clamped_glu ? clamped_glu(g, u) : g / (1.0f + __expf(-g)) * u;
+            hout[int64_t(row0 + row) * p.I + pos] = (_Float16)hv;
+          }
         }
       }
     }
   } else {
     float* y = reinterpret_cast<float*>(p.out);
+    if (!p.bias) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
+      for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (row < rows) {
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (row < rows) {
 #pragma unroll
-          for (int f = 0; f < 2; ++f)
-            if (nvalid[f]) y[int64_t(row0 + row) * p.N + nrow[f]] = acc[rb][f][r];
+            for (int f = 0; f < 2; ++f)
+              if (nvalid[f]) y[int64_t(row0 + row) * p.N + nrow[f]] = acc[rb][f][r];
+          }
+        }
+      }
+    } else {
+      float bn[2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) bn[f] = p.bias[int64_t(e) * p.N + nrow[f]];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (row < rows) {
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+              if (nvalid[f]) y[int64_t(row0 + row) * p.N + nrow[f]] = acc[rb][f][r] + bn[f];
+          }
         }
       }
     }
@@ -526,6 +565,8 @@ template <int FMT, int BM, int WAVES>
 static hipError_t launch_gemms(const MoeLaunch& L, hipStream_t stream) {
   GemmArgs g{};
   g.slots = L.slots;
+  g.clamped_glu = L.clamped_glu;
+  g.interleaved = L.interleaved;
   g.k_top = L.k;
   g.I = L.I;
   g.T = L.T;
@@ -534,6 +575,7 @@ static hipError_t launch_gemms(const MoeLaunch& L, hipStream_t stream) {
   g.wq = L.w_gu;
   g.sc = L.s_gu;
   g.out = L.h;
+  g.bias = L.b_gu;
   g.K = L.H;
   g.N = 2 * L.I;
   hipError_t err = launch_stage_tiles<FMT, true, BM, WAVES>(L, g, stream);
@@ -541,6 +583,7 @@ static hipError_t launch_gemms(const MoeLaunch& L, hipStream_t stream) {
   record(L, 3, stream);
   // down + routing weight
   g.a = L.h;
+  g.bias = L.b_dn;
   g.wq = L.w_dn;
   g.sc = L.s_dn;
   g.out = L.y;

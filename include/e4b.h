@@ -76,6 +76,15 @@ typedef enum e4b_fmt { E4B_FMT_NF4 = 0, E4B_FMT_MXFP4 = 1 } e4b_fmt;
 #define E4B_TILE_128 0x8
 #define E4B_TILE_256 0xC
 #define E4B_TILE_MASK 0xC
+/* e4b_moe_args.flags bits 4-5: expert variant of the MXFP4 model family with per-expert
+ * biases and a clamped GLU (experts4bit-qlora 0.35.0 project description, Scope; the pages
+ * give no formula, so the family's own definition is taken).  Any format may use them.
+ *   E4B_ACT_CLAMPED_GLU  h = min(G,7) * sigmoid(1.702 * min(G,7)) * (clamp(U,-7,7) + 1)
+ *                        instead of h = silu(G) * U
+ *   E4B_GU_INTERLEAVED   gate_up rows interleaved: row 2j is gate j, row 2j+1 is up j
+ *                        (default: rows 0..I-1 gate, I..2I-1 up) */
+#define E4B_ACT_CLAMPED_GLU 0x10
+#define E4B_GU_INTERLEAVED 0x20
 
 /*
  * e4b_pack_nf4 — quantise bf16 expert stacks to NF4.
@@ -150,6 +159,10 @@ typedef struct e4b_moe_args {
    * tile map, gate_up GEMM, down GEMM, combine), so a caller can time each kernel on the
    * stream it runs on.  Events are created and owned by the caller. */
   void* const* stage_events;
+  /* NULL, or [E, 2I] float32 bias added to each gate_up product (same row order as w_gu),
+   * and NULL, or [E, H] float32 bias added to each down product before the weighted sum. */
+  const float* b_gu;
+  const float* b_dn;
 } e4b_moe_args;
 
 /* Workspace bytes e4b_moe_forward needs for the sizes, format and flags in `a`. */

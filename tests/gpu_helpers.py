@@ -83,18 +83,24 @@ class Layer:
     def route(self, renormalize=True):
         return self.e4b.e4b_route_permute(self.logits_dev, self.k, renormalize)
 
-    def forward(self, path=0, route=None):
+    def forward(self, path=0, route=None, act="swiglu", interleaved=False, b_gu=None, b_dn=None):
         ids, w, off, slots = route if route is not None else self.route()
+        dev = lambda b: None if b is None else torch.from_numpy(np.ascontiguousarray(b, np.float32)).to(DEV)
         out, out32 = self.e4b.e4b_moe_forward(self.fmt, self.x, self.gp, self.gs, self.dp, self.ds,
-                                              w, off, slots, self.k, out_f32=True, path=path)
+                                              w, off, slots, self.k, out_f32=True, path=path,
+                                              act=act, interleaved=interleaved,
+                                              b_gu=dev(b_gu), b_dn=dev(b_dn))
         torch.cuda.synchronize()
         return host(out), host(out32)
 
-    def oracle_out(self, tokens=None):
+    def oracle_out(self, tokens=None, act="swiglu", interleaved=False, b_gu=None, b_dn=None):
         gp, gs = oracle_pack(self.fmt, self.gu_bits)
         dp, ds = oracle_pack(self.fmt, self.dn_bits)
         ids, w, *_ = oroute.route(self.logits, self.k)
-        return omoe.forward(self.fmt, self.x_bits, gp, gs, dp, ds, ids, w, tokens)
+        # the GPU adds float32 biases: the oracle gets the same float32 values
+        f32 = lambda b: None if b is None else np.asarray(b, np.float32).astype(np.float64)
+        return omoe.forward(self.fmt, self.x_bits, gp, gs, dp, ds, ids, w, tokens, act=act,
+                            interleaved=interleaved, b_gu=f32(b_gu), b_dn=f32(b_dn))
 
 
 def random_layer(e4b, fmt, E, H, I, T, k, seed, wscale=0.02, logit_bias=None):

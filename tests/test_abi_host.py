@@ -102,7 +102,8 @@ def test_forward_rejects_bad_arguments(e4b):
     assert f(E=0) == ERR_ARG
     assert f(T=-1) == ERR_ARG
     assert f(flags=3) == ERR_ARG
-    assert f(flags=0x10) == ERR_ARG
+    assert f(flags=0x40) == ERR_ARG                  # unknown bit
+    assert f(flags=0x30) not in (ERR_ARG, ERR_SHAPE)   # expert-variant bits are accepted
     assert f(flags=7) == ERR_ARG
     assert f(flags=0x6) == ERR_ARG                   # tile override with the streaming path
     assert f(H=96) == ERR_SHAPE
@@ -112,6 +113,8 @@ def test_forward_rejects_bad_arguments(e4b):
     assert f(ws=None) == ERR_ARG
     assert f(out=FAKE + 2) == ERR_ALIGN
     assert f(out_f32=FAKE + 4) == ERR_ALIGN
+    assert f(b_gu=FAKE + 4) == ERR_ALIGN
+    assert f(b_dn=FAKE + 8) == ERR_ALIGN
     assert f(ws_bytes=1024) == ERR_WORKSPACE
     assert f(T=1 << 28, k=8) == ERR_OVERFLOW
     assert f(T=1 << 20, H=1 << 12) == ERR_OVERFLOW

@@ -142,3 +142,42 @@ def test_graph_replay_matches_eager(e4b, path):
         step()  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(out32, ref)
+
+
+# ------------------------------------------------- clamped-GLU / interleaved / bias variant
+
+VARIANT_CASES = [
+    # fmt, flags (path | tile), E, H, I, T, k
+    ("mxfp4", 0x0, 8, 256, 256, 300, 2),    # automatic: 128-row tiles, tail tiles
+    ("nf4", 0xC, 2, 256, 256, 270, 2),      # 256-row tiles + streaming tail tiles (slot order)
+    ("mxfp4", 0xC, 2, 256, 320, 270, 2),    # the same in MXFP4 (natural order tails)
+    ("nf4", 0x4, 4, 256, 256, 64, 2),       # 32-row tiles
+    ("mxfp4", 0x2, 16, 256, 256, 16, 4),    # streaming path
+    ("nf4", 0x0, 16, 512, 256, 8, 4),       # automatic: streaming path
+]
+
+
+@pytest.mark.parametrize("fmt,flags,E,H,I,T,k", VARIANT_CASES)
+def test_clamped_glu_interleaved_with_biases(e4b, fmt, flags, E, H, I, T, k):
+    layer = random_layer(e4b, fmt, E, H, I, T, k, seed=E * 7 + T + (flags << 4))
+    rng = np.random.default_rng(T + E)
+    # biases wide enough that some gate values pass the clamp at 7 and some up values leave [-7, 7]
+    b_gu = (4.0 * rng.standard_normal((E, 2 * I))).astype(np.float32)
+    b_dn = rng.standard_normal((E, H)).astype(np.float32)
+    for interleaved in (True, False):
+        out, out32 = layer.forward(flags, act="clamped_glu", interleaved=interleaved, b_gu=b_gu, b_dn=b_dn)
+        ref = layer.oracle_out(act="clamped_glu", interleaved=interleaved, b_gu=b_gu, b_dn=b_dn)
+        assert_rows_within_tolerance(out32, ref, f"{fmt} flags={flags:#x} interleaved={interleaved}")
+        assert_out_is_rne_of_f32(out, out32)
+
+
+@pytest.mark.parametrize("flags", [0x0, 0x2])
+def test_swiglu_with_one_bias_and_interleaved_rows(e4b, flags):
+    E, H, I, T, k = 8, 256, 256, 48 if flags == 0x2 else 400, 2
+    layer = random_layer(e4b, "nf4", E, H, I, T, k, seed=31 + flags)
+    rng = np.random.default_rng(5)
+    b_gu = rng.standard_normal((E, 2 * I)).astype(np.float32)
+    b_dn = rng.standard_normal((E, H)).astype(np.float32)
+    for kw in (dict(b_gu=b_gu), dict(b_dn=b_dn), dict(interleaved=True, b_gu=b_gu)):
+        out, out32 = layer.forward(flags, **kw)
+        assert_rows_within_tolerance(out32, layer.oracle_out(**kw), f"flags={flags:#x} {sorted(kw)}")
