@@ -350,7 +350,20 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
     }
   } else {
     float* y = reinterpret_cast<float*>(p.out);
-    if (!p.bias) {
+    const bool full = rows == BM && int64_t(nt + 1) * (WAVES * 64) <= p.N;  // uniform
+    if (!p.bias && full) {
+      // a full tile: no per-element guards, so the stores issue back to back
+      float* yb = y + int64_t(row0) * p.N;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3);
+#pragma unroll
+          for (int f = 0; f < 2; ++f) yb[int64_t(row) * p.N + nrow[f]] = acc[rb][f][r];
+        }
+      }
+    } else if (!p.bias) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
