@@ -9,7 +9,8 @@ moe_inputs.py.  Prints ONE JSON line on stdout; progress goes to stderr.
 
 The headline workload is the Mixtral-shaped NF4 prefill layer (E=8, H=4096, I=14336, top-2,
 T=4096).  The same line carries, under "secondary", the skewed 64-expert prefill layer, the
-MXFP4 layer and the 128-expert decode layer at T = 64, 16, 4, 1 (warm, and cold with the
+MXFP4 layer (also run as the MXFP4 family's expert variant: interleaved gate/up rows, clamped
+GLU, per-expert biases) and the 128-expert decode layer at T = 64, 16, 4, 1 (warm, and cold with the
 256 MB Infinity Cache flushed by reading 1 GiB before every step; eager launches with per-stage HIP events,
 and the same step replayed from a HIP graph), and a float64 CPU-oracle baseline timed on a
 bounded sample of the headline workload.
@@ -29,7 +30,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from moe_inputs import WORKLOADS, make_expert_weight, make_logits, make_x  # noqa: E402
+from moe_inputs import WORKLOADS, make_bias, make_expert_weight, make_logits, make_x  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD published
 PEAK_F16_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, AMD published
@@ -78,6 +79,7 @@ class Batch:
     """x, router logits and every output / workspace buffer of one batch size."""
 
     flags = 0
+    variant = {}  # expert-variant keyword arguments of e4b_moe_forward (act, interleaved, biases)
 
     def __init__(self, layer: Layer, T: int):
         torch, e4b = layer.torch, layer.e4b
@@ -102,7 +104,7 @@ class Batch:
         gp, gs = self.layer.packed["gate_up"]
         dp, ds = self.layer.packed["down"]
         self.e4b.e4b_moe_forward(wl.fmt, self.x, gp, gs, dp, ds, w, off, slots, wl.k, out=self.out,
-                                 ws=self.fwd_ws, stage_events=events, path=self.flags)
+                                 ws=self.fwd_ws, stage_events=events, path=self.flags, **self.variant)
         return off
 
     def active_experts(self) -> int:
@@ -297,9 +299,10 @@ def blas_threads() -> str:
 
 
 def batch_report(torch, layer: Layer, T: int, steps: int, warmup: int, flush: int = 0, flags: int = 0,
-                 graph: bool = False):
+                 graph: bool = False, variant: dict | None = None):
     b = Batch(layer, T)
     b.flags = flags
+    b.variant = variant or {}
     wl = b.wl
     n_active = b.active_experts()
     m = measure(torch, b, steps, warmup, flush)
@@ -372,6 +375,17 @@ def main():
             lay = Layer(e4b, torch, WORKLOADS[name])
             secondary[name] = batch_report(torch, lay, WORKLOADS[name].T, max(args.steps, 10), args.warmup)
             log(fmt_rep(name, secondary[name]))
+            if name == "mxfp4_moe":
+                # the same layer as the MXFP4 family's expert variant: gate/up rows read as
+                # interleaved, clamped GLU, the seeded biases of moe_inputs.make_bias
+                wv = WORKLOADS[name]
+                variant = dict(act="clamped_glu", interleaved=True,
+                               b_gu=torch.from_numpy(make_bias(wv, "gate_up")).to("cuda:0"),
+                               b_dn=torch.from_numpy(make_bias(wv, "down")).to("cuda:0"))
+                key = name + "_clamped_glu"
+                secondary[key] = batch_report(torch, lay, wv.T, max(args.steps, 10), args.warmup,
+                                              variant=variant)
+                log(fmt_rep(key, secondary[key]))
             del lay
             torch.cuda.empty_cache()
         dwl = WORKLOADS["finegrained_nf4_decode"]

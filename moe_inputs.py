@@ -7,13 +7,15 @@ CPU oracle receive the arrays produced here.
 
 Recipe (one generator stream per tensor and per expert, so experts can be drawn one at a
 time):  ``rng(tid, e) = numpy.random.default_rng(SeedSequence([seed, tid, e]))`` with
-tid 0 = x, 1 = router logits, 2 = gate_up, 3 = down.
+tid 0 = x, 1 = router logits, 2 = gate_up, 3 = down, 4 = gate_up bias, 5 = down bias.
 
 * x      = bf16_rne(N(0, 1) float32 draws), shape [T, H]
 * W      = bf16_rne(0.02 * N(0, 1) float32 draws), per expert, shape [N, K]
            (gate_up: N = 2I, K = H; down: N = H, K = I)
 * logits = N(0, 1) float32 draws, shape [T, E]; the skewed workload adds
            float32(2 * ln(w_r)) with w_r = r^-1.2 / sum_{r'=1..E} r'^-1.2, rank r = e + 1.
+* biases (expert variant only) = float32(0.02 * N(0, 1) float32 draws): gate_up [E, 2I],
+           down [E, H], one stream per tensor.
 """
 from __future__ import annotations
 
@@ -23,7 +25,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-TID_X, TID_LOGITS, TID_GATE_UP, TID_DOWN = 0, 1, 2, 3
+TID_X, TID_LOGITS, TID_GATE_UP, TID_DOWN, TID_B_GU, TID_B_DN = 0, 1, 2, 3, 4, 5
 
 
 @dataclasses.dataclass(frozen=True)
@@ -105,6 +107,19 @@ def make_expert_weight(wl: Workload, which: str, e: int) -> np.ndarray:
     g = _rng(wl.seed, tid, e).standard_normal(shape, dtype=np.float32)
     g *= np.float32(0.02)
     return f32_to_bf16_bits(g)
+
+
+def make_bias(wl: Workload, which: str) -> np.ndarray:
+    """float32 biases of the expert variant: gate_up [E, 2I] or down [E, H]."""
+    if which == "gate_up":
+        tid, shape = TID_B_GU, (wl.E, 2 * wl.I)
+    elif which == "down":
+        tid, shape = TID_B_DN, (wl.E, wl.H)
+    else:
+        raise ValueError(which)
+    g = _rng(wl.seed, tid).standard_normal(shape, dtype=np.float32)
+    g *= np.float32(0.02)
+    return g
 
 
 def make_weights(wl: Workload, which: str, experts=None, threads: int = 8) -> np.ndarray:

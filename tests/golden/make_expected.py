@@ -20,13 +20,14 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, os.path.dirname(os.path.dirname(HERE)))
 
-from moe_inputs import WORKLOADS, make_expert_weight, make_logits, make_x  # noqa: E402
+from moe_inputs import WORKLOADS, make_bias, make_expert_weight, make_logits, make_x  # noqa: E402
 from oracle import moe as omoe  # noqa: E402
 from oracle import mxfp4 as omx  # noqa: E402
 from oracle import nf4 as onf4  # noqa: E402
 from oracle import route as oroute  # noqa: E402
 
-# (case name, workload, T override or None)
+# (case name, workload, T override or None); a "_clamped_glu" case is the expert variant
+# (interleaved gate/up rows, clamped GLU, seeded biases of moe_inputs.make_bias)
 CASES = [
     ("mixtral_nf4_prefill", "mixtral_nf4_prefill", None),
     ("finegrained_nf4_decode_T1", "finegrained_nf4_decode", 1),
@@ -35,6 +36,7 @@ CASES = [
     ("finegrained_nf4_decode_T64", "finegrained_nf4_decode", 64),
     ("mxfp4_moe", "mxfp4_moe", None),
     ("skewed_nf4_prefill", "skewed_nf4_prefill", None),
+    ("mxfp4_moe_clamped_glu", "mxfp4_moe", None),
 ]
 N_SAMPLE = 6
 
@@ -59,7 +61,12 @@ def expected(case: str, name: str, T):
         e = int(e)
         gp[e], gs[e] = q.quantize_pack(make_expert_weight(wl, "gate_up", e))
         dp[e], ds[e] = q.quantize_pack(make_expert_weight(wl, "down", e))
-    out = omoe.forward(wl.fmt, x_bits, gp, gs, dp, ds, ids, w, toks)
+    kw = {}
+    if case.endswith("_clamped_glu"):
+        kw = dict(act="clamped_glu", interleaved=True,
+                  b_gu=make_bias(wl, "gate_up").astype(np.float64),
+                  b_dn=make_bias(wl, "down").astype(np.float64))
+    out = omoe.forward(wl.fmt, x_bits, gp, gs, dp, ds, ids, w, toks, **kw)
     return {"tokens": toks, "ids": ids[toks].astype(np.int32), "w": w[toks].astype(np.float64),
             "out": out}
 

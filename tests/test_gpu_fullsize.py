@@ -15,7 +15,7 @@ import pytest
 import torch
 
 from gpu_helpers import assert_out_is_rne_of_f32, assert_rows_within_tolerance, bf16_violations, host
-from moe_inputs import WORKLOADS, make_expert_weight, make_logits, make_x
+from moe_inputs import WORKLOADS, make_bias, make_expert_weight, make_logits, make_x
 
 pytestmark = pytest.mark.gpu
 
@@ -29,6 +29,7 @@ CASES = [
     ("finegrained_nf4_decode_T64", "finegrained_nf4_decode", 64),
     ("mxfp4_moe", "mxfp4_moe", None),
     ("skewed_nf4_prefill", "skewed_nf4_prefill", None),
+    ("mxfp4_moe_clamped_glu", "mxfp4_moe", None),   # expert variant, same packed layer
 ]
 
 _packed_cache = {}
@@ -65,7 +66,12 @@ def test_full_size_sampled_tokens(e4b, case, name, T, record_property):
     ids, w, off, slots = e4b.e4b_route_permute(logits, wl.k)
     gp, gs = packed["gate_up"]
     dp, ds = packed["down"]
-    out, out32 = e4b.e4b_moe_forward(wl.fmt, x, gp, gs, dp, ds, w, off, slots, wl.k, out_f32=True)
+    kw = {}
+    if case.endswith("_clamped_glu"):
+        kw = dict(act="clamped_glu", interleaved=True,
+                  b_gu=torch.from_numpy(make_bias(wl, "gate_up")).to(DEV),
+                  b_dn=torch.from_numpy(make_bias(wl, "down")).to(DEV))
+    out, out32 = e4b.e4b_moe_forward(wl.fmt, x, gp, gs, dp, ds, w, off, slots, wl.k, out_f32=True, **kw)
     torch.cuda.synchronize()
     toks = exp["tokens"]
     # routing of the sampled tokens: ids bit-exact, weights to fp32 precision
