@@ -122,3 +122,25 @@ def f64_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     u = np.asarray(a, np.float64).astype(np.float32).view(np.uint32)
     r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return r.astype(np.uint16)
+
+
+def dgrad(fmt: str, packed: np.ndarray, scales: np.ndarray, g_bits: np.ndarray,
+          offsets: np.ndarray) -> np.ndarray:
+    """Grouped input gradient on the packed stacks, float64: for every expert e and each row p
+    of its block [offsets[e], offsets[e+1]) of the grouped rows, out[p] = g[p] @ W_e, where
+    W_e [N, K] is the decoded weight and g [S, N] the bf16 gradient of the expert's output.
+
+    The transposed product of the forward step y = x W_e^T (Cerin Amroth "ML systems" index,
+    Ownership: the kernels package owns the grouped packed GEMM and its dgrad): the same
+    packed bytes, contracted over their row index N instead of K.
+    """
+    g = bf16_bits_to_f64(np.asarray(g_bits))
+    S = g.shape[0]
+    K = (packed.shape[2] * 2) if fmt == "nf4" else packed.shape[2] * 32
+    out = np.zeros((S, K), np.float64)
+    offsets = np.asarray(offsets, np.int64)
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            out[lo:hi] = g[lo:hi] @ decode_expert(fmt, packed, scales, e)
+    return out
