@@ -16,7 +16,7 @@ __all__ = [
     "E4BError", "E4B_FMT_NF4", "E4B_FMT_MXFP4", "E4B_PATH_AUTO", "E4B_PATH_GEMM", "E4B_PATH_GEMV",
     "E4B_ROUTE_RENORMALIZE", "E4B_ACT_CLAMPED_GLU", "E4B_GU_INTERLEAVED", "lib_path", "e4b_version", "e4b_status_string", "e4b_pack_nf4",
     "e4b_pack_mxfp4", "e4b_route_workspace_bytes", "e4b_route_permute", "e4b_moe_workspace_bytes",
-    "e4b_moe_forward", "MoeArgs",
+    "e4b_moe_forward", "MoeArgs", "e4b_dgrad_workspace_bytes", "e4b_grouped_dgrad", "DgradArgs",
 ]
 
 E4B_FMT_NF4, E4B_FMT_MXFP4 = 0, 1
@@ -49,6 +49,15 @@ class MoeArgs(ctypes.Structure):
     ]
 
 
+class DgradArgs(ctypes.Structure):
+    """Mirror of struct e4b_dgrad_args."""
+    _fields_ = [
+        ("fmt", _i32), ("reserved", _i32), ("E", _i64), ("N", _i64), ("K", _i64), ("S", _i64),
+        ("g", _vp), ("w", _vp), ("s", _vp), ("expert_offsets", _vp), ("out_f32", _vp), ("out", _vp),
+        ("ws", _vp), ("ws_bytes", _sz),
+    ]
+
+
 def _decl(name, argtypes, restype=ctypes.c_int):
     fn = getattr(_lib, name)
     fn.argtypes = argtypes
@@ -64,6 +73,8 @@ _c_route_ws = _decl("e4b_route_workspace_bytes", [_i64, _i64, _i32, ctypes.POINT
 _c_route = _decl("e4b_route_permute", [_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
 _c_moe_ws = _decl("e4b_moe_workspace_bytes", [ctypes.POINTER(MoeArgs), ctypes.POINTER(_sz)])
 _c_moe_forward = _decl("e4b_moe_forward", [ctypes.POINTER(MoeArgs), _vp])
+_c_dgrad_ws = _decl("e4b_dgrad_workspace_bytes", [ctypes.POINTER(DgradArgs), ctypes.POINTER(_sz)])
+_c_dgrad = _decl("e4b_grouped_dgrad", [ctypes.POINTER(DgradArgs), _vp])
 
 
 class E4BError(RuntimeError):
@@ -234,3 +245,48 @@ def e4b_moe_forward(fmt, x, w_gu, s_gu, w_dn, s_dn, topk_w, expert_offsets, sort
         a.stage_events = ctypes.cast(handles, ctypes.POINTER(_vp))
     _check("e4b_moe_forward", _c_moe_forward(ctypes.byref(a), _stream(stream)))
     return out, out_f32
+
+
+def _dgrad_args(fmt, E, N, K, S) -> DgradArgs:
+    a = DgradArgs()
+    a.fmt, a.E, a.N, a.K, a.S = _FMT[fmt], E, N, K, S
+    return a
+
+
+def e4b_dgrad_workspace_bytes(fmt, E: int, N: int, K: int, S: int) -> int:
+    n = _sz(0)
+    _check("e4b_dgrad_workspace_bytes", _c_dgrad_ws(ctypes.byref(_dgrad_args(fmt, E, N, K, S)), ctypes.byref(n)))
+    return n.value
+
+
+def e4b_grouped_dgrad(fmt, g, w, s, expert_offsets, out_f32=None, out=False, ws=None, stream=None):
+    """Grouped dgrad on a packed stack: out[p] = g[p] @ W_e for the rows p of expert e.
+
+    g: [S, N] bf16 (rows grouped by expert); w, s: a packed stack as returned by
+    e4b_pack_nf4 / e4b_pack_mxfp4 ([E, N, K/2] | [E, N, K/32, 16] and its scales);
+    expert_offsets [E+1] int32.  Returns (out_f32 [S, K], out bf16 [S, K] or None); pass
+    out=True to get the bf16 copy.
+    """
+    _need(g, "g", _BF16)
+    S, N = g.shape
+    E = w.shape[0]
+    K = w.shape[2] * (2 if w.dim() == 3 else 32)
+    if w.shape[1] != N:
+        raise ValueError(f"w has {w.shape[1]} rows per expert, g has {N} columns")
+    _need(expert_offsets, "expert_offsets", (torch.int32,), (E + 1,))
+    dev = g.device
+    if out_f32 is None:
+        out_f32 = torch.empty((S, K), dtype=torch.float32, device=dev)
+    if out is True:
+        out = torch.empty((S, K), dtype=torch.bfloat16, device=dev)
+    elif out is False:
+        out = None
+    if ws is None:
+        ws = torch.empty((max(e4b_dgrad_workspace_bytes(fmt, E, N, K, S), 256),), dtype=torch.uint8, device=dev)
+    a = _dgrad_args(fmt, E, N, K, S)
+    a.g, a.w, a.s, a.expert_offsets = g.data_ptr(), w.data_ptr(), s.data_ptr(), expert_offsets.data_ptr()
+    a.out_f32 = out_f32.data_ptr()
+    a.out = None if out is None else out.data_ptr()
+    a.ws, a.ws_bytes = ws.data_ptr(), ws.numel() * ws.element_size()
+    _check("e4b_grouped_dgrad", _c_dgrad(ctypes.byref(a), _stream(stream)))
+    return out_f32, out

@@ -124,11 +124,68 @@ int check_forward_shape(const e4b_moe_args* a) {
   return E4B_OK;
 }
 
+int dgrad_check(const e4b_dgrad_args* a, int64_t* max_tiles) {
+  if (!a) return E4B_ERR_ARG;
+  if (a->fmt != E4B_FMT_NF4 && a->fmt != E4B_FMT_MXFP4) return E4B_ERR_ARG;
+  if (a->reserved != 0) return E4B_ERR_ARG;
+  if (a->E <= 0 || a->N <= 0 || a->K <= 0 || a->S < 0) return E4B_ERR_ARG;
+  if (a->N % 64 || a->K % 64) return E4B_ERR_SHAPE;
+  if (a->E > 1024 * 1024 || a->S * a->N >= (int64_t(1) << 31) || a->S * a->K >= (int64_t(1) << 31) ||
+      a->N * (a->K / 2) >= (int64_t(1) << 31))
+    return E4B_ERR_OVERFLOW;
+  const int64_t bm = e4b::dgrad_tile_rows();
+  const int64_t active = a->E < a->S ? a->E : a->S;
+  *max_tiles = (a->S + active * (bm - 1)) / bm;
+  return E4B_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-int e4b_version(void) { return 200; }
+int e4b_version(void) { return 300; }
+
+
+int e4b_dgrad_workspace_bytes(const e4b_dgrad_args* a, size_t* bytes) {
+  if (!bytes) return E4B_ERR_ARG;
+  int64_t mt = 0;
+  const int st = dgrad_check(a, &mt);
+  if (st != E4B_OK) return st;
+  *bytes = align_up(size_t(mt) * 16) + kAlign;
+  return E4B_OK;
+}
+
+int e4b_grouped_dgrad(const e4b_dgrad_args* a, void* stream) {
+  int64_t mt = 0;
+  int st = dgrad_check(a, &mt);
+  if (st != E4B_OK) return st;
+  if (a->S == 0) return check_device();
+  if (!a->g || !a->w || !a->s || !a->expert_offsets || !a->out_f32 || !a->ws) return E4B_ERR_ARG;
+  const void* ptrs[] = {a->g, a->w, a->s, a->expert_offsets, a->out_f32, a->out, a->ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return E4B_ERR_ALIGN;
+  size_t need = 0;
+  e4b_dgrad_workspace_bytes(a, &need);
+  if (a->ws_bytes < need) return E4B_ERR_WORKSPACE;
+  if ((st = check_device()) != E4B_OK) return st;
+  char* ws = reinterpret_cast<char*>(a->ws);
+  e4b::DgradLaunch L{};
+  L.fmt = a->fmt;
+  L.E = a->E;
+  L.N = a->N;
+  L.K = a->K;
+  L.S = a->S;
+  L.g = a->g;
+  L.wq = a->w;
+  L.sc = a->s;
+  L.offsets = a->expert_offsets;
+  L.out_f32 = a->out_f32;
+  L.out = a->out;
+  L.tiles = reinterpret_cast<int32_t*>(ws);
+  L.n_tiles = reinterpret_cast<int32_t*>(ws + align_up(size_t(mt) * 16));
+  L.max_tiles = mt;
+  return launched(e4b::launch_dgrad(L, (hipStream_t)stream));
+}
 
 const char* e4b_status_string(int status) {
   switch (status) {

@@ -65,6 +65,27 @@ struct MoeLaunch {
 
 hipError_t launch_moe_forward(const MoeLaunch& L, hipStream_t stream);
 
+// The tile list of build_tiles as its own launch (bm-row tiles, no tail tiles).
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, int32_t* tiles,
+                              int32_t* n_tiles, hipStream_t stream);
+
+// Grouped dgrad: out[p] = g[p] @ W_e for the grouped rows p of expert e.
+struct DgradLaunch {
+  int fmt;
+  int64_t E, N, K, S;
+  const uint16_t* g;
+  const uint8_t* wq;
+  const void* sc;
+  const int32_t* offsets;
+  float* out_f32;
+  uint16_t* out;        // nullable
+  int32_t* tiles;       // workspace [max_tiles, 4]
+  int32_t* n_tiles;     // workspace [2]
+  int64_t max_tiles;
+};
+hipError_t launch_dgrad(const DgradLaunch& L, hipStream_t stream);
+int dgrad_tile_rows();
+
 // Small-M streaming kernels: stage 0 = gate_up + SwiGLU (x16 -> h), 1 = down (h -> y).
 hipError_t launch_gemv(const MoeLaunch& L, hipStream_t stream, int stage);
 // The same kernels over the tail tiles of the MFMA-tile path (its activation order).

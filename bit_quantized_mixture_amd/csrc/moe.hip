@@ -485,6 +485,15 @@ __device__ void build_tiles(const TileArgs& ta) {
   }
 }
 
+__global__ void __launch_bounds__(256) build_tiles_kernel(TileArgs ta) { build_tiles(ta); }
+
+hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, int32_t* tiles,
+                              int32_t* n_tiles, hipStream_t stream) {
+  const TileArgs ta{offsets, E, bm, 0, tiles, tiles, n_tiles};
+  hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, stream, ta);
+  return hipGetLastError();
+}
+
 // x bf16 -> fp16 (exact for |x| in fp16's normal range), stored in the k-slot order of the
 // weight format inside each aligned group of 8.  Also inverts the routing permutation,
 // inv[slots[p]] = p for the S sorted rows p, and records each sorted row's token,

@@ -180,6 +180,36 @@ int e4b_moe_workspace_bytes(const e4b_moe_args* a, size_t* bytes);
  */
 int e4b_moe_forward(const e4b_moe_args* a, void* stream);
 
+/* Arguments of e4b_grouped_dgrad. */
+typedef struct e4b_dgrad_args {
+  int32_t fmt;            /* e4b_fmt */
+  int32_t reserved;       /* must be 0 */
+  int64_t E, N, K;        /* packed stack [E, N, K] (as packed by e4b_pack_*); N % 64 == 0, K % 64 == 0 */
+  int64_t S;              /* grouped rows: expert_offsets[E] */
+  const uint16_t* g;      /* [S, N] bf16 bits, rows grouped by expert; values in fp16 range */
+  const uint8_t* w;       /* NF4 [E, N, K/2] | MXFP4 [E, N, K/32, 16] */
+  const void* s;          /* NF4 float [E, N, K/64] | MXFP4 uint8 [E, N, K/32] */
+  const int32_t* expert_offsets; /* [E+1]: rows of expert e are offsets[e] .. offsets[e+1]-1 */
+  float* out_f32;         /* [S, K] float32 out */
+  uint16_t* out;          /* [S, K] bf16 out (RNE of out_f32), or NULL */
+  void* ws;               /* device workspace of at least e4b_dgrad_workspace_bytes() */
+  size_t ws_bytes;
+} e4b_dgrad_args;
+
+/* Workspace bytes e4b_grouped_dgrad needs for the sizes in `a`. */
+int e4b_dgrad_workspace_bytes(const e4b_dgrad_args* a, size_t* bytes);
+
+/*
+ * e4b_grouped_dgrad — the input gradient of the grouped expert product on the packed
+ * stacks (Cerin Amroth "ML systems" index, Ownership: the grouped packed GEMM and its dgrad):
+ * out[p, :] = g[p, :] @ W_e for every row p of expert e's block, W_e the decoded [N, K]
+ * weight.  For gate_up (N = 2I, K = H) g is the gradient of the gate/up products and out
+ * the gradient of x's grouped copies; for down (N = H, K = I) g is the gradient of y.
+ * fp16 operands (g converted exactly from bf16, weights decoded to fp16) with fp32
+ * accumulation; deterministic.  Synchronous errors as e4b_moe_forward.
+ */
+int e4b_grouped_dgrad(const e4b_dgrad_args* a, void* stream);
+
 /* Static description of a status code. */
 const char* e4b_status_string(int status);
 

@@ -22,7 +22,8 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("e4b_pack_nf4", "e4b_pack_mxfp4", "e4b_route_permute", "e4b_moe_forward",
-              "e4b_route_workspace_bytes", "e4b_moe_workspace_bytes", "e4b_status_string", "e4b_version"):
+              "e4b_route_workspace_bytes", "e4b_moe_workspace_bytes", "e4b_status_string", "e4b_version",
+              "e4b_dgrad_workspace_bytes", "e4b_grouped_dgrad"):
         assert n in names
 
 
@@ -127,3 +128,27 @@ def test_workspace_sizes_cover_the_intermediates(e4b):
         S = wl.T * wl.k
         assert n >= 2 * wl.T * wl.H + 2 * S * wl.I + 4 * S * wl.H
         assert n < 2 * (2 * wl.T * wl.H + 2 * S * wl.I + 4 * S * wl.H) + (1 << 20)
+
+
+def test_dgrad_rejects_bad_arguments(e4b):
+    def f(**kw):
+        a = e4b.DgradArgs()
+        a.fmt, a.E, a.N, a.K, a.S = 0, 4, 128, 256, 100
+        for n in ("g", "w", "s", "expert_offsets", "out_f32", "ws"):
+            setattr(a, n, FAKE)
+        a.ws_bytes = 1 << 40
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return e4b._c_dgrad(ctypes.byref(a), None)
+    assert f(fmt=3) == ERR_ARG
+    assert f(E=0) == ERR_ARG
+    assert f(S=-1) == ERR_ARG
+    assert f(reserved=1) == ERR_ARG
+    assert f(N=96) == ERR_SHAPE
+    assert f(K=100) == ERR_SHAPE
+    assert f(g=None) == ERR_ARG
+    assert f(out_f32=None) == ERR_ARG
+    assert f(out=FAKE + 2) == ERR_ALIGN
+    assert f(ws_bytes=16) == ERR_WORKSPACE
+    assert f(S=1 << 24, N=1 << 10) == ERR_OVERFLOW
+    assert e4b.e4b_dgrad_workspace_bytes("nf4", 4, 128, 256, 100) >= 64
