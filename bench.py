@@ -13,7 +13,8 @@ MXFP4 layer (also run as the MXFP4 family's expert variant: interleaved gate/up 
 GLU, per-expert biases) and the 128-expert decode layer at T = 64, 16, 4, 1 (warm, and cold with the
 256 MB Infinity Cache flushed by reading 1 GiB before every step; eager launches with per-stage HIP events,
 and the same step replayed from a HIP graph), and a float64 CPU-oracle baseline timed on a
-bounded sample of the headline workload.
+bounded sample of the headline workload.  Also under "secondary": the grouped dgrad on the
+headline layer's packed down and gate_up stacks with its own routing.
 """
 from __future__ import annotations
 
@@ -327,6 +328,46 @@ def batch_report(torch, layer: Layer, T: int, steps: int, warmup: int, flush: in
     return rep
 
 
+def dgrad_report(torch, layer: Layer, steps: int, warmup: int) -> dict:
+    """Grouped dgrad on the layer's packed stacks, with the layer's own routing: down
+    (g [S, H] -> [S, I]) and gate_up (g [S, 2I] -> [S, H]); seeded bf16 N(0, 1) gradients.
+    Timed with HIP events on the current stream (one launch each, after warm-up)."""
+    e4b, wl = layer.e4b, layer.wl
+    b = Batch(layer, wl.T)
+    off = b.step()
+    S = wl.T * wl.k
+    g_gen = torch.Generator(device="cuda:0").manual_seed(1)
+    rep = {}
+    for which, N, K in (("down", wl.H, wl.I), ("gate_up", 2 * wl.I, wl.H)):
+        w, sc = layer.packed[which]
+        g = torch.randn((S, N), generator=g_gen, device="cuda:0").to(torch.bfloat16)
+        out = torch.empty((S, K), dtype=torch.float32, device="cuda:0")
+        ws = torch.empty((max(e4b.e4b_dgrad_workspace_bytes(wl.fmt, wl.E, N, K, S), 256),),
+                         dtype=torch.uint8, device="cuda:0")
+        run = lambda: e4b.e4b_grouped_dgrad(wl.fmt, g, w, sc, off, out_f32=out, ws=ws)
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        gc.collect()
+        gc.disable()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            run()
+        t1.record()
+        torch.cuda.synchronize()
+        gc.enable()
+        ms = t0.elapsed_time(t1) / steps
+        flops = 2.0 * S * N * K
+        tf = flops / (ms / 1e3) / 1e12
+        rep[which] = {"ms": ms, "tflops": tf, "frac_of_mfma_peak": tf / PEAK_F16_MFMA_TFLOPS,
+                      "algorithmic_flops": flops, "S": S, "N": N, "K": K}
+        del g, out, ws
+    del b
+    torch.cuda.empty_cache()
+    return rep
+
+
 def fmt_rep(key, rep):
     rl = rep["roofline"]
     s = (f"[bench] {key}: {rep['ms_per_step']:.4f} ms/step, {rep['tokens_per_s']:.0f} tok/s, "
@@ -364,10 +405,14 @@ def main():
     pack_gbs = layer.pack_bytes / layer.pack_s / 1e9
     main_rep = batch_report(torch, layer, wl.T, args.steps, args.warmup, flags=args.flags)
     log(fmt_rep(wl.name, main_rep) + f"; stages {main_rep['stage_ms']}")
+    secondary = {}
+    if not args.no_secondary:
+        secondary[wl.name + "_dgrad"] = dg = dgrad_report(torch, layer, max(args.steps, 10), args.warmup)
+        log(f"[bench] {wl.name} dgrad: " + ", ".join(
+            f"{k} {v['ms']:.3f} ms {v['tflops']:.1f} TFLOP/s ({100 * v['frac_of_mfma_peak']:.1f}%)" for k, v in dg.items()))
     del layer
     torch.cuda.empty_cache()
 
-    secondary = {}
     if not args.no_secondary:
         for name in ("skewed_nf4_prefill", "mxfp4_moe"):
             if name == wl.name:
