@@ -6,12 +6,14 @@
 // The contraction now runs over the weight rows n, while a packed row is contiguous along k,
 // so the MFMA operand that needs 8 consecutive n for one k cannot be read from a row.  Each
 // K step (32 weight rows) is decoded cooperatively and written to LDS transposed, [k][n]
-// fp16, with a padded row pitch; the gradient tile goes to LDS as [row][n] fp16.  Both are
+// fp16, in a padded, swizzled layout; the gradient tile goes to LDS as [row][n] fp16.  Both are
 // double-buffered with one workgroup barrier per step.
 //
-// Workgroup: 4 waves, a tile of <= 128 grouped rows of one expert x 256 columns k; wave w owns
-// columns 64w .. 64w + 63 (two 32-column fragments) for all 128 rows, fp32 accumulators in
-// registers (v_mfma_f32_32x32x16_f16, four row blocks x two fragments).
+// Workgroup: 8 waves (two per SIMD), a tile of <= 256 grouped rows of one expert x 256
+// columns k; wave w owns rows 128(w/4) .. +127 and columns 64(w%4) .. +63 (four 32-row blocks x
+// two 32-column fragments, fp32 accumulators in registers, v_mfma_f32_32x32x16_f16), so each
+// decoded weight feeds 256 rows.  The global loads of a step are issued two steps ahead of its
+// staging (two register sets) with per-step offsets in scalar registers.
 #include "e4b_device.h"
 #include "e4b_internal.h"
 
@@ -19,13 +21,23 @@ namespace e4b {
 
 namespace {
 
-constexpr int kRows = 128;           // grouped rows per tile
+constexpr int kThreads = 512;
+constexpr int kRows = 256;           // grouped rows per tile
 constexpr int kCols = 256;           // output columns k per workgroup
 constexpr int kStepN = 32;           // weight rows n per step
-constexpr int kPitch = 80;           // LDS row pitch in bytes (64 data + 16 pad: 16-lane
-                                     // groups of 16-byte reads hit distinct banks)
-constexpr int kGBytes = kRows * kPitch;   // gradient tile [128][32] fp16
-constexpr int kWBytes = kCols * kPitch;   // transposed weight tile [256][32] fp16
+
+// LDS tile layout, shared by both tiles: a tile row (a grouped row of the gradient, or a column
+// k of the weights) holds the step's 32 n values in fp16 as four 16-byte chunks.  Rows are 64
+// bytes apart plus 64 bytes after every 8 rows, and chunk j of row r sits in slot
+// j ^ ((r >> 2) & 3).  Then the 16-byte fragment reads (16 consecutive rows, one chunk), the
+// 16-byte gradient writes and the 4-byte transposed weight writes (rows 8 apart, 16 n-pairs)
+// each spread over all 64 banks without conflicts.
+__device__ __forceinline__ int lds_off(int r, int j) {
+  return 64 * r + 64 * (r >> 3) + 16 * (j ^ ((r >> 2) & 3));
+}
+constexpr int tile_bytes(int rows) { return 64 * rows + 64 * (rows / 8); }
+constexpr int kGBytes = tile_bytes(kRows);   // gradient tile [256][32] fp16
+constexpr int kWBytes = tile_bytes(kCols);   // transposed weight tile [256][32] fp16
 constexpr int kBufBytes = kGBytes + kWBytes;
 
 struct DgradArgs {
@@ -40,58 +52,71 @@ struct DgradArgs {
   int32_t n_ktiles;
 };
 
-// Element e (0..7) of a decoded dword sits in output register kReg[e], half kHi[e]: NF4's
-// register decode leaves slot order (0,2) (4,6) (1,3) (5,7), MXFP4 natural order.
+// Element e (0..7) of a decoded dword sits in output register elem_reg(e), half elem_hi(e):
+// NF4's register decode leaves slot order (0,2) (4,6) (1,3) (5,7), MXFP4 natural order.
 template <int FMT>
 __device__ __forceinline__ int elem_reg(int e) { return FMT == 0 ? ((e & 1) ? 2 + (e >> 2) : (e >> 2)) : (e >> 1); }
 template <int FMT>
 __device__ __forceinline__ int elem_hi(int e) { return FMT == 0 ? ((e >> 1) & 1) : (e & 1); }
 
+// Global loads of one step for one thread: two 16-byte gradient pieces, two packed dwords and
+// their two scales.
+struct StepRegs {
+  u32x4 g[2];
+  uint32_t w[2], s[2];
+};
+
 template <int FMT>
-__global__ void __launch_bounds__(256) dgrad_kernel(DgradArgs p) {
+__global__ void __launch_bounds__(kThreads) dgrad_kernel(DgradArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kBufBytes];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
+  const int rh = wave >> 2, wcol = wave & 3;
   const int kt = int(blockIdx.x) % p.n_ktiles;
   const int mt = int(blockIdx.x) / p.n_ktiles;
   if (mt >= *p.n_tiles) return;  // uniform
   const int e = p.tiles[4 * mt], row0 = p.tiles[4 * mt + 1], rows = p.tiles[4 * mt + 2];
   const int64_t kbytes = p.K >> 1;
-  const int nsteps = int(p.N / kStepN);
+  const int nsteps = int(p.N / kStepN);  // even: N is a multiple of 64
 
-  // ---- staging roles.  Gradient: thread t loads row t/2, n half (t&1)*16 (two 16-byte
-  // loads of 8 bf16).  Weights: thread t decodes rows 4q..4q+3 (q = t/32) of the step at
-  // column chunk c = t%32 (8 columns = one packed dword per row).
+  // ---- staging roles.  Gradient: thread t loads row t/2, chunks 2(t&1) and 2(t&1) + 1 (16
+  // n values).  Weights: thread t decodes rows 2q, 2q + 1 (q = t%16) of the step at column
+  // chunk c = 4(t/64) + (t%64)/16 (8 columns = one packed dword per row).
   const int grow = tid >> 1, gh = tid & 1;
   const int grow_c = grow < rows ? grow : rows - 1;
-  const uint16_t* gsrc = p.g + int64_t(row0 + grow_c) * p.N + 16 * gh;
-  const int wq4 = tid >> 5, wc = tid & 31;
+  const __amdgpu_buffer_rsrc_t gres =
+      buffer_rsrc(p.g + int64_t(row0) * p.N, uint32_t(int64_t(rows) * p.N * 2));
+  const uint32_t goff = uint32_t(grow_c) * uint32_t(p.N) * 2u + 32u * gh;
+  const int wq2 = lane & 15, wc = 4 * wave + (lane >> 4);
   const int64_t kcol0 = int64_t(kt) * kCols + 8 * wc;       // first column of the chunk
   const bool wvalid = kcol0 < p.K;
-  const uint32_t wbyte = uint32_t(wvalid ? (kcol0 >> 1) : 0);
+  const uint32_t nblk = uint32_t(FMT == 0 ? (p.K >> 6) : (p.K >> 5));  // scale blocks per row
+  const uint32_t sblk = wvalid ? uint32_t(FMT == 0 ? (kcol0 >> 6) : (kcol0 >> 5)) : 0u;
   const __amdgpu_buffer_rsrc_t wres =
       buffer_rsrc(p.wq + int64_t(e) * p.N * kbytes, uint32_t(p.N * kbytes));
-  const int64_t nblk = FMT == 0 ? (p.K >> 6) : (p.K >> 5);  // scale blocks per row
-  const int64_t sblk = wvalid ? (FMT == 0 ? (kcol0 >> 6) : (kcol0 >> 5)) : 0;
+  const uint32_t woff = uint32_t(2 * wq2) * uint32_t(kbytes) + uint32_t(wvalid ? (kcol0 >> 1) : 0);
+  constexpr uint32_t kScaleBytes = FMT == 0 ? 4u : 1u;
+  const __amdgpu_buffer_rsrc_t sres =
+      buffer_rsrc(static_cast<const uint8_t*>(p.sc) + int64_t(e) * p.N * nblk * kScaleBytes,
+                  uint32_t(p.N * nblk * kScaleBytes));
+  const uint32_t soff = (uint32_t(2 * wq2) * nblk + sblk) * kScaleBytes;
 
-  u32x4 gv[2];
-  uint32_t wv[4], sv[4];
-  auto load_step = [&](int s) {
-    const int n0 = s * kStepN;
+  auto load_step = [&](int s, StepRegs& R) {
+    const uint32_t n0 = uint32_t(s * kStepN);  // uniform: the step's offsets go in SGPRs
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      gv[i] = *reinterpret_cast<const u32x4*>(gsrc + n0 + 8 * i);
+      R.g[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(gres, goff + 16u * i, 2u * n0, 0));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t n = n0 + 4 * wq4 + r;
-      wv[r] = __builtin_amdgcn_raw_buffer_load_b32(wres, uint32_t(n * kbytes) + wbyte, 0, 0);
+    for (int r = 0; r < 2; ++r) {
+      R.w[r] = __builtin_amdgcn_raw_buffer_load_b32(wres, woff + uint32_t(r) * uint32_t(kbytes),
+                                                     n0 * uint32_t(kbytes), 0);
       if (FMT == 0)
-        sv[r] = __float_as_uint(reinterpret_cast<const float*>(p.sc)[(int64_t(e) * p.N + n) * nblk + sblk]);
+        R.s[r] = __builtin_amdgcn_raw_buffer_load_b32(sres, soff + uint32_t(r) * nblk * 4u, n0 * nblk * 4u, 0);
       else
-        sv[r] = reinterpret_cast<const uint8_t*>(p.sc)[(int64_t(e) * p.N + n) * nblk + sblk];
+        R.s[r] = __builtin_amdgcn_raw_buffer_load_b8(sres, soff + uint32_t(r) * nblk, n0 * nblk, 0);
     }
   };
-  auto stage_step = [&](int buf) {
+  auto stage_step = [&](const StepRegs& R, int buf) {
     uint8_t* gb = smem + buf * kBufBytes;
     uint8_t* wb = gb + kGBytes;
     // gradient: bf16 -> fp16 (exact in fp16's normal range)
@@ -100,55 +125,47 @@ __global__ void __launch_bounds__(256) dgrad_kernel(DgradArgs p) {
       f16x8 h;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        h[2 * j] = (_Float16)__uint_as_float(gv[i][j] << 16);
-        h[2 * j + 1] = (_Float16)__uint_as_float(gv[i][j] & 0xFFFF0000u);
+        h[2 * j] = (_Float16)__uint_as_float(R.g[i][j] << 16);
+        h[2 * j + 1] = (_Float16)__uint_as_float(R.g[i][j] & 0xFFFF0000u);
       }
-      *reinterpret_cast<f16x8*>(gb + grow * kPitch + 32 * gh + 16 * i) = h;
+      *reinterpret_cast<f16x8*>(gb + lds_off(grow, 2 * gh + i)) = h;
     }
-    // weights: decode 4 rows x 8 columns, write each column's 4 rows as one 8-byte word
-    uint32_t d[4][4];
+    // weights: decode 2 rows x 8 columns, write each column's 2 rows as one 4-byte word
+    uint32_t d[2][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < 2; ++r) {
       if (FMT == 0) {
-        nf4_decode8(wv[r], d[r]);
-        const float scf = __uint_as_float(sv[r]);
+        nf4_decode8(R.w[r], d[r]);
+        const float scf = __uint_as_float(R.s[r]);
         const f16x2 s16 = f16x2{(_Float16)scf, (_Float16)scf};
 #pragma unroll
         for (int i = 0; i < 4; ++i) d[r][i] = pk_mul_f16(d[r][i], s16);
       } else {
-        mxfp4_decode8(wv[r], e8m0_to_f32(sv[r]), d[r]);
+        mxfp4_decode8(R.w[r], e8m0_to_f32(R.s[r]), d[r]);
       }
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int reg = elem_reg<FMT>(c), hi = elem_hi<FMT>(c);
-      const uint32_t sel = hi ? 0x07060302u : 0x05040100u;
-      const uint32_t lo01 = perm(d[1][reg], d[0][reg], sel);
-      const uint32_t lo23 = perm(d[3][reg], d[2][reg], sel);
-      *reinterpret_cast<u32x2*>(wb + (8 * wc + c) * kPitch + 8 * wq4) = u32x2{lo01, lo23};
+      const uint32_t v = perm(d[1][reg], d[0][reg], hi ? 0x07060302u : 0x05040100u);
+      *reinterpret_cast<uint32_t*>(wb + lds_off(8 * wc + c, wq2 >> 2) + 4 * (wq2 & 3)) = v;
     }
   };
-  // A fragment: rows 32rb + col, n 16sub + 8half .. +7; B fragment: column 64wave + 32f + col.
+  // A fragment: rows 128rh + 32rb + col, n 16sub + 8half .. +7; B fragment: column
+  // 64wcol + 32f + col.
   auto afrag = [&](int buf, int rb, int sub) {
-    return *reinterpret_cast<const f16x8*>(smem + buf * kBufBytes + (32 * rb + col) * kPitch +
-                                           32 * sub + 16 * half);
+    return *reinterpret_cast<const f16x8*>(smem + buf * kBufBytes +
+                                           lds_off(128 * rh + 32 * rb + col, 2 * sub + half));
   };
   auto bfrag = [&](int buf, int f, int sub) {
     return *reinterpret_cast<const f16x8*>(smem + buf * kBufBytes + kGBytes +
-                                           (64 * wave + 32 * f + col) * kPitch + 32 * sub + 16 * half);
+                                           lds_off(64 * wcol + 32 * f + col, 2 * sub + half));
   };
 
   f32x16 acc[4][2];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) acc[rb][0] = acc[rb][1] = f32x16{};
-
-  load_step(0);
-  stage_step(0);
-  __syncthreads();
-  for (int s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    const bool more = s + 1 < nsteps;  // uniform
-    if (more) load_step(s + 1);
+  auto mfma_step = [&](int buf) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const f16x8 b0 = bfrag(buf, 0, sub), b1 = bfrag(buf, 1, sub);
@@ -158,22 +175,42 @@ __global__ void __launch_bounds__(256) dgrad_kernel(DgradArgs p) {
         acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b0, acc[rb][0], 0, 0, 0);
         acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b1, acc[rb][1], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // the other buffer was last read in step s - 1, before the previous barrier
-    if (more) stage_step(buf ^ 1);
+  };
+
+  // Register set A holds the even steps' loads, B the odd ones'.  Loads past the last step
+  // repeat the last step and the last staging writes a buffer nobody reads any more: both keep
+  // the loop body branch-free and the wait counts the same every pass.
+  StepRegs A, B;
+  load_step(0, A);
+  load_step(1, B);
+  stage_step(A, 0);
+  load_step(nsteps > 2 ? 2 : nsteps - 1, A);
+  __syncthreads();
+  for (int s = 0; s < nsteps; s += 2) {
+    // step s in buffer 0; B holds step s + 1, A step s + 2
+    mfma_step(0);
+    stage_step(B, 1);  // buffer 1 was last read in step s - 1, before the previous barrier
+    load_step(s + 3 < nsteps ? s + 3 : nsteps - 1, B);
+    __syncthreads();
+    // step s + 1 in buffer 1; A holds step s + 2, B step s + 3
+    mfma_step(1);
+    stage_step(A, 0);
+    load_step(s + 4 < nsteps ? s + 4 : nsteps - 1, A);
     __syncthreads();
   }
 
   // ---- epilogue.  Accumulator element r of a 32x32 block: row 8(r/4) + 4half + r%4.
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
-    const int64_t k = int64_t(kt) * kCols + 64 * wave + 32 * f + col;
+    const int64_t k = int64_t(kt) * kCols + 64 * wcol + 32 * f + col;
     if (k >= p.K) continue;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int row = 128 * rh + 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3);
         if (row < rows) {
           const int64_t o = int64_t(row0 + row) * p.K + k;
           const float v = acc[rb][f][r];
@@ -203,9 +240,9 @@ hipError_t launch_dgrad(const DgradLaunch& L, hipStream_t stream) {
   a.n_ktiles = int((L.K + kCols - 1) / kCols);
   const unsigned grid = unsigned(L.max_tiles * a.n_ktiles);
   if (L.fmt == 0)
-    hipLaunchKernelGGL(dgrad_kernel<0>, dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(dgrad_kernel<0>, dim3(grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(dgrad_kernel<1>, dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(dgrad_kernel<1>, dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
