@@ -26,14 +26,18 @@ constexpr int kRows = 256;           // grouped rows per tile
 constexpr int kCols = 256;           // output columns k per workgroup
 constexpr int kStepN = 32;           // weight rows n per step
 
-// LDS tile layout, shared by both tiles: a tile row (a grouped row of the gradient, or a column
-// k of the weights) holds the step's 32 n values in fp16 as four 16-byte chunks.  Rows are 64
-// bytes apart plus 64 bytes after every 8 rows, and chunk j of row r sits in slot
-// j ^ ((r >> 2) & 3).  Then the 16-byte fragment reads (16 consecutive rows, one chunk), the
-// 16-byte gradient writes and the 4-byte transposed weight writes (rows 8 apart, 16 n-pairs)
-// each spread over all 64 banks without conflicts.
+// LDS tile layout: a tile row (a grouped row of the gradient, or a column k of the weights)
+// holds the step's 32 n values in fp16 as four 16-byte chunks.  Rows are 64 bytes apart plus
+// 64 bytes after every 8 rows, and chunk j of row r sits in slot j ^ ((r >> 2) & 3) (gradient)
+// or j ^ (((r >> 2) ^ (r >> 5)) & 3) (weights).  Then the 16-byte fragment reads (16
+// consecutive rows, one chunk), the 16-byte gradient writes (whole rows) and the 4-byte
+// transposed weight writes (4 n-pairs x 16 columns 8 apart) each spread over all 64 banks
+// without conflicts.
 __device__ __forceinline__ int lds_off(int r, int j) {
   return 64 * r + 64 * (r >> 3) + 16 * (j ^ ((r >> 2) & 3));
+}
+__device__ __forceinline__ int lds_off_w(int r, int j) {
+  return 64 * r + 64 * (r >> 3) + 16 * (j ^ (((r >> 2) ^ (r >> 5)) & 3));
 }
 constexpr int tile_bytes(int rows) { return 64 * rows + 64 * (rows / 8); }
 constexpr int kGBytes = tile_bytes(kRows);   // gradient tile [256][32] fp16
@@ -79,15 +83,19 @@ __global__ void __launch_bounds__(kThreads) dgrad_kernel(DgradArgs p) {
   const int64_t kbytes = p.K >> 1;
   const int nsteps = int(p.N / kStepN);  // even: N is a multiple of 64
 
-  // ---- staging roles.  Gradient: thread t loads row t/2, chunks 2(t&1) and 2(t&1) + 1 (16
-  // n values).  Weights: thread t decodes rows 2q, 2q + 1 (q = t%16) of the step at column
-  // chunk c = 4(t/64) + (t%64)/16 (8 columns = one packed dword per row).
-  const int grow = tid >> 1, gh = tid & 1;
-  const int grow_c = grow < rows ? grow : rows - 1;
+  // ---- staging roles.  Gradient: thread t loads chunk t%4 (8 n values) of rows t/4 and
+  // t/4 + 128, so 16 consecutive lanes fill 4 whole tile rows (256 contiguous LDS bytes).
+  // Weights: lane l of wave w decodes rows 2q, 2q + 1 (q = 4(w%4) + l/16) of the step at
+  // column chunk c = 16(w/4) + l%16 (8 columns = one packed dword per row), so one load covers
+  // 64 contiguous bytes of each of 4 rows.
+  const int grow = tid >> 2, gj = tid & 3;
+  const int grow0_c = grow < rows ? grow : rows - 1;
+  const int grow1_c = grow + kThreads / 4 < rows ? grow + kThreads / 4 : rows - 1;
   const __amdgpu_buffer_rsrc_t gres =
       buffer_rsrc(p.g + int64_t(row0) * p.N, uint32_t(int64_t(rows) * p.N * 2));
-  const uint32_t goff = uint32_t(grow_c) * uint32_t(p.N) * 2u + 32u * gh;
-  const int wq2 = lane & 15, wc = 4 * wave + (lane >> 4);
+  const uint32_t goff0 = uint32_t(grow0_c) * uint32_t(p.N) * 2u + 16u * gj;
+  const uint32_t goff1 = uint32_t(grow1_c) * uint32_t(p.N) * 2u + 16u * gj;
+  const int wq2 = 4 * (wave & 3) + (lane >> 4), wc = 16 * (wave >> 2) + (lane & 15);
   const int64_t kcol0 = int64_t(kt) * kCols + 8 * wc;       // first column of the chunk
   const bool wvalid = kcol0 < p.K;
   const uint32_t nblk = uint32_t(FMT == 0 ? (p.K >> 6) : (p.K >> 5));  // scale blocks per row
@@ -101,19 +109,27 @@ __global__ void __launch_bounds__(kThreads) dgrad_kernel(DgradArgs p) {
                   uint32_t(p.N * nblk * kScaleBytes));
   const uint32_t soff = (uint32_t(2 * wq2) * nblk + sblk) * kScaleBytes;
 
+  // The loads of a step are issued in one fixed order everywhere (scheduling barriers between
+  // them): the wait-count pass merges the prologue's and the loop's states at the loop header
+  // and can only keep its counts tight if both issued the loads in the same order.
   auto load_step = [&](int s, StepRegs& R) {
     const uint32_t n0 = uint32_t(s * kStepN);  // uniform: the step's offsets go in SGPRs
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      R.g[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(gres, goff + 16u * i, 2u * n0, 0));
+    for (int i = 0; i < 2; ++i) {
+      R.g[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(gres, i ? goff1 : goff0, 2u * n0, 0));
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       R.w[r] = __builtin_amdgcn_raw_buffer_load_b32(wres, woff + uint32_t(r) * uint32_t(kbytes),
                                                      n0 * uint32_t(kbytes), 0);
+      __builtin_amdgcn_sched_barrier(0);
       if (FMT == 0)
         R.s[r] = __builtin_amdgcn_raw_buffer_load_b32(sres, soff + uint32_t(r) * nblk * 4u, n0 * nblk * 4u, 0);
       else
         R.s[r] = __builtin_amdgcn_raw_buffer_load_b8(sres, soff + uint32_t(r) * nblk, n0 * nblk, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   auto stage_step = [&](const StepRegs& R, int buf) {
@@ -128,7 +144,7 @@ __global__ void __launch_bounds__(kThreads) dgrad_kernel(DgradArgs p) {
         h[2 * j] = (_Float16)__uint_as_float(R.g[i][j] << 16);
         h[2 * j + 1] = (_Float16)__uint_as_float(R.g[i][j] & 0xFFFF0000u);
       }
-      *reinterpret_cast<f16x8*>(gb + lds_off(grow, 2 * gh + i)) = h;
+      *reinterpret_cast<f16x8*>(gb + lds_off(grow + i * (kThreads / 4), gj)) = h;
     }
     // weights: decode 2 rows x 8 columns, write each column's 2 rows as one 4-byte word
     uint32_t d[2][4];
@@ -148,7 +164,7 @@ __global__ void __launch_bounds__(kThreads) dgrad_kernel(DgradArgs p) {
     for (int c = 0; c < 8; ++c) {
       const int reg = elem_reg<FMT>(c), hi = elem_hi<FMT>(c);
       const uint32_t v = perm(d[1][reg], d[0][reg], hi ? 0x07060302u : 0x05040100u);
-      *reinterpret_cast<uint32_t*>(wb + lds_off(8 * wc + c, wq2 >> 2) + 4 * (wq2 & 3)) = v;
+      *reinterpret_cast<uint32_t*>(wb + lds_off_w(8 * wc + c, wq2 >> 2) + 4 * (wq2 & 3)) = v;
     }
   };
   // A fragment: rows 128rh + 32rb + col, n 16sub + 8half .. +7; B fragment: column
@@ -159,24 +175,45 @@ __global__ void __launch_bounds__(kThreads) dgrad_kernel(DgradArgs p) {
   };
   auto bfrag = [&](int buf, int f, int sub) {
     return *reinterpret_cast<const f16x8*>(smem + buf * kBufBytes + kGBytes +
-                                           lds_off(64 * wcol + 32 * f + col, 2 * sub + half));
+                                           lds_off_w(64 * wcol + 32 * f + col, 2 * sub + half));
   };
 
   f32x16 acc[4][2];
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) acc[rb][0] = acc[rb][1] = f32x16{};
-  auto mfma_step = [&](int buf) {
+  auto read_sub = [&](int buf, int sub, f16x8 (&a)[4], f16x8 (&b)[2]) {
+    b[0] = bfrag(buf, 0, sub);
+    b[1] = bfrag(buf, 1, sub);
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const f16x8 b0 = bfrag(buf, 0, sub), b1 = bfrag(buf, 1, sub);
+    for (int rb = 0; rb < 4; ++rb) a[rb] = afrag(buf, rb, sub);
+  };
+  auto mma = [&](const f16x8 (&a)[4], const f16x8 (&b)[2]) {
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const f16x8 a = afrag(buf, rb, sub);
-        acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b0, acc[rb][0], 0, 0, 0);
-        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b1, acc[rb][1], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int rb = 0; rb < 4; ++rb) {
+      acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[rb], b[0], acc[rb][0], 0, 0, 0);
+      acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[rb], b[1], acc[rb][1], 0, 0, 0);
     }
+  };
+  // One step: all twelve fragment reads of the step go out first, into distinct registers, so
+  // the LDS latency is paid once per step; the staging of the next step into the other buffer
+  // is woven between the MFMAs (both waves of a SIMD leave the barrier together, so the MFMA
+  // pipe and the VALU only overlap if each wave interleaves them itself).
+  auto step = [&](int buf, const StepRegs& R) {
+    f16x8 a0[4], b0[2], a1[4], b1[2];
+    __builtin_amdgcn_sched_barrier(0);
+    read_sub(buf, 0, a0, b0);
+    read_sub(buf, 1, a1, b1);
+    mma(a0, b0);
+    mma(a1, b1);
+    stage_step(R, buf ^ 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // DS read: all fragments
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      if (i >= 6) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // Register set A holds the even steps' loads, B the odd ones'.  Loads past the last step
@@ -186,17 +223,16 @@ __global__ void __launch_bounds__(kThreads) dgrad_kernel(DgradArgs p) {
   load_step(0, A);
   load_step(1, B);
   stage_step(A, 0);
+  __builtin_amdgcn_sched_barrier(0);
   load_step(nsteps > 2 ? 2 : nsteps - 1, A);
   __syncthreads();
   for (int s = 0; s < nsteps; s += 2) {
     // step s in buffer 0; B holds step s + 1, A step s + 2
-    mfma_step(0);
-    stage_step(B, 1);  // buffer 1 was last read in step s - 1, before the previous barrier
+    step(0, B);  // buffer 1 was last read in step s - 1, before the previous barrier
     load_step(s + 3 < nsteps ? s + 3 : nsteps - 1, B);
     __syncthreads();
     // step s + 1 in buffer 1; A holds step s + 2, B step s + 3
-    mfma_step(1);
-    stage_step(A, 0);
+    step(1, A);
     load_step(s + 4 < nsteps ? s + 4 : nsteps - 1, A);
     __syncthreads();
   }
