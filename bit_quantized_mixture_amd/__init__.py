@@ -58,6 +58,15 @@ class DgradArgs(ctypes.Structure):
     ]
 
 
+class Int4GemvArgs(ctypes.Structure):
+    """Mirror of struct e4b_int4_gemv_args."""
+    _fields_ = [
+        ("E", _i64), ("N", _i64), ("K", _i64), ("T", _i64), ("k", _i32), ("reserved", _i32),
+        ("x", _vp), ("w", _vp), ("s", _vp), ("expert_offsets", _vp), ("sorted_slots", _vp),
+        ("out_f32", _vp), ("ws", _vp), ("ws_bytes", _sz),
+    ]
+
+
 def _decl(name, argtypes, restype=ctypes.c_int):
     fn = getattr(_lib, name)
     fn.argtypes = argtypes
@@ -75,6 +84,10 @@ _c_moe_ws = _decl("e4b_moe_workspace_bytes", [ctypes.POINTER(MoeArgs), ctypes.PO
 _c_moe_forward = _decl("e4b_moe_forward", [ctypes.POINTER(MoeArgs), _vp])
 _c_dgrad_ws = _decl("e4b_dgrad_workspace_bytes", [ctypes.POINTER(DgradArgs), ctypes.POINTER(_sz)])
 _c_dgrad = _decl("e4b_grouped_dgrad", [ctypes.POINTER(DgradArgs), _vp])
+_c_pack_int4 = _decl("e4b_pack_int4_b32", [_vp, _i64, _i64, _i64, _vp, _vp, _vp])
+_c_quant_act = _decl("e4b_quantize_act_int8", [_vp, _i64, _i64, _vp, _vp, _vp])
+_c_int4_ws = _decl("e4b_int4_gemv_workspace_bytes", [ctypes.POINTER(Int4GemvArgs), ctypes.POINTER(_sz)])
+_c_int4_gemv = _decl("e4b_gemv_int4_b32", [ctypes.POINTER(Int4GemvArgs), _vp])
 
 
 class E4BError(RuntimeError):
@@ -290,3 +303,68 @@ def e4b_grouped_dgrad(fmt, g, w, s, expert_offsets, out_f32=None, out=False, ws=
     a.ws, a.ws_bytes = ws.data_ptr(), ws.numel() * ws.element_size()
     _check("e4b_grouped_dgrad", _c_dgrad(ctypes.byref(a), _stream(stream)))
     return out_f32, out
+
+
+def e4b_pack_int4_b32(w, packed=None, scales=None, stream=None):
+    """w [E, N, K] bf16 -> (packed uint8 [E, N, K/2], scales float16 [E, N, K/32])."""
+    _need(w, "w", _BF16)
+    E, N, K = w.shape
+    if packed is None:
+        packed = torch.empty((E, N, K // 2), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((E, N, K // 32), dtype=torch.float16, device=w.device)
+    _check("e4b_pack_int4_b32", _c_pack_int4(_ptr(w), E, N, K, _ptr(packed), _ptr(scales), _stream(stream)))
+    return packed, scales
+
+
+def e4b_quantize_act_int8(x, stream=None):
+    """x [T, K] bf16 -> (q int8 [T, K], s float32 [T]): per-token int8 activations."""
+    _need(x, "x", _BF16)
+    T, K = x.shape
+    q = torch.empty((T, K), dtype=torch.int8, device=x.device)
+    sc = torch.empty((max(T, 1),), dtype=torch.float32, device=x.device)[:T]
+    _check("e4b_quantize_act_int8", _c_quant_act(_ptr(x), T, K, _ptr(q), _ptr(sc), _stream(stream)))
+    return q, sc
+
+
+def _int4_args(E, N, K, T, k):
+    a = Int4GemvArgs()
+    a.E, a.N, a.K, a.T, a.k, a.reserved = E, N, K, T, k, 0
+    return a
+
+
+def e4b_int4_gemv_workspace_bytes(E: int, N: int, K: int, T: int, k: int) -> int:
+    n = _sz(0)
+    _check("e4b_int4_gemv_workspace_bytes",
+           _c_int4_ws(ctypes.byref(_int4_args(E, N, K, T, k)), ctypes.byref(n)))
+    return n.value
+
+
+def e4b_gemv_int4_b32(w, s, x, k: int, expert_offsets, sorted_slots, out=None, ws=None, stream=None):
+    """Routed int4-b32 decode GEMV with exact integer accumulation.
+
+    w [E, N, K/2] uint8 and s [E, N, K/32] float16 from e4b_pack_int4_b32; x [T, K] bf16;
+    expert_offsets [E+1] and sorted_slots [T*k] int32 from e4b_route_permute.  Returns
+    out [T*k, N] float32 in sorted-row order (row p: token sorted_slots[p] // k through the
+    expert whose offsets contain p).
+    """
+    _need(x, "x", _BF16)
+    T, K = x.shape
+    _need(w, "w", (torch.uint8,))
+    E, N = w.shape[0], w.shape[1]
+    _need(w, "w", (torch.uint8,), (E, N, K // 2))
+    _need(s, "s", (torch.float16, torch.int16), (E, N, K // 32))
+    _need(expert_offsets, "expert_offsets", (torch.int32,), (E + 1,))
+    _need(sorted_slots, "sorted_slots", (torch.int32,), (T * k,))
+    if out is None:
+        out = torch.empty((T * k, N), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = torch.empty((max(e4b_int4_gemv_workspace_bytes(E, N, K, T, k), 256),),
+                         dtype=torch.uint8, device=x.device)
+    a = _int4_args(E, N, K, T, k)
+    a.x, a.w, a.s = x.data_ptr(), w.data_ptr(), s.data_ptr()
+    a.expert_offsets, a.sorted_slots = expert_offsets.data_ptr(), sorted_slots.data_ptr()
+    a.out_f32 = out.data_ptr()
+    a.ws, a.ws_bytes = ws.data_ptr(), ws.numel() * ws.element_size()
+    _check("e4b_gemv_int4_b32", _c_int4_gemv(ctypes.byref(a), _stream(stream)))
+    return out

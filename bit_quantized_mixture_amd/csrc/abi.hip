@@ -139,9 +139,98 @@ int dgrad_check(const e4b_dgrad_args* a, int64_t* max_tiles) {
   return E4B_OK;
 }
 
+int int4_check(const e4b_int4_gemv_args* a, int64_t* max_tiles) {
+  if (!a) return E4B_ERR_ARG;
+  if (a->reserved != 0) return E4B_ERR_ARG;
+  if (a->E <= 0 || a->N <= 0 || a->K <= 0 || a->T < 0 || a->k < 1 || a->k > 64 || a->k > a->E)
+    return E4B_ERR_ARG;
+  if (a->N % 16 || a->K % 128 || a->K > 8192) return E4B_ERR_SHAPE;
+  const int64_t S = a->T * a->k;
+  if (a->E > 1024 * 1024 || a->T >= (int64_t(1) << 31) || S >= (int64_t(1) << 31) ||
+      S * a->N >= (int64_t(1) << 40) || a->N * (a->K / 2) >= (int64_t(1) << 31))
+    return E4B_ERR_OVERFLOW;
+  const int64_t bm = a->T > 0 ? e4b::int4_gemv_tile_rows(a->T) : 1;
+  const int64_t active = a->E < S ? a->E : S;
+  *max_tiles = (S + active * (bm - 1)) / bm;
+  return E4B_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int e4b_pack_int4_b32(const uint16_t* w, int64_t E, int64_t N, int64_t K, uint8_t* packed,
+                      uint16_t* scales, void* stream) {
+  if (!w || !packed || !scales || E <= 0 || N <= 0 || K <= 0) return E4B_ERR_ARG;
+  if (K % 32) return E4B_ERR_SHAPE;
+  if (!aligned16(w) || !aligned16(packed) || !aligned16(scales)) return E4B_ERR_ALIGN;
+  if (E > (int64_t(1) << 40) / N / K) return E4B_ERR_OVERFLOW;
+  const int st = check_device();
+  if (st != E4B_OK) return st;
+  return launched(e4b::launch_pack_int4(w, E * N * K, packed, scales, (hipStream_t)stream));
+}
+
+int e4b_quantize_act_int8(const uint16_t* x, int64_t T, int64_t K, int8_t* q, float* s,
+                          void* stream) {
+  if (!x || !q || !s || T < 0 || K <= 0) return E4B_ERR_ARG;
+  if (K % 32) return E4B_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return E4B_ERR_ALIGN;
+  if (T >= (int64_t(1) << 31) || K >= (int64_t(1) << 31)) return E4B_ERR_OVERFLOW;
+  const int st = check_device();
+  if (st != E4B_OK || T == 0) return st;
+  return launched(e4b::launch_quant_act(x, T, K, q, s, nullptr, (hipStream_t)stream));
+}
+
+int e4b_int4_gemv_workspace_bytes(const e4b_int4_gemv_args* a, size_t* bytes) {
+  if (!bytes) return E4B_ERR_ARG;
+  int64_t mt = 0;
+  const int st = int4_check(a, &mt);
+  if (st != E4B_OK) return st;
+  *bytes = align_up(size_t(a->T * a->K)) + align_up(size_t(a->T * (a->K / 32) * 4)) +
+           align_up(size_t(a->T * 4)) + align_up(size_t(mt) * 16) + kAlign;
+  return E4B_OK;
+}
+
+int e4b_gemv_int4_b32(const e4b_int4_gemv_args* a, void* stream) {
+  int64_t mt = 0;
+  int st = int4_check(a, &mt);
+  if (st != E4B_OK) return st;
+  if (a->T == 0) return check_device();
+  if (!a->x || !a->w || !a->s || !a->expert_offsets || !a->sorted_slots || !a->out_f32 || !a->ws)
+    return E4B_ERR_ARG;
+  const void* ptrs[] = {a->x, a->w, a->s, a->expert_offsets, a->sorted_slots, a->out_f32, a->ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return E4B_ERR_ALIGN;
+  size_t need = 0;
+  e4b_int4_gemv_workspace_bytes(a, &need);
+  if (a->ws_bytes < need) return E4B_ERR_WORKSPACE;
+  if ((st = check_device()) != E4B_OK) return st;
+  char* ws = reinterpret_cast<char*>(a->ws);
+  e4b::Int4GemvLaunch L{};
+  L.E = a->E;
+  L.N = a->N;
+  L.K = a->K;
+  L.T = a->T;
+  L.k = a->k;
+  L.x = a->x;
+  L.wq = a->w;
+  L.sc = a->s;
+  L.offsets = a->expert_offsets;
+  L.slots = a->sorted_slots;
+  L.out = a->out_f32;
+  size_t off = 0;
+  L.qx = reinterpret_cast<int8_t*>(ws + off);
+  off += align_up(size_t(a->T * a->K));
+  L.xs = reinterpret_cast<int32_t*>(ws + off);
+  off += align_up(size_t(a->T * (a->K / 32) * 4));
+  L.sx = reinterpret_cast<float*>(ws + off);
+  off += align_up(size_t(a->T * 4));
+  L.tiles = reinterpret_cast<int32_t*>(ws + off);
+  off += align_up(size_t(mt) * 16);
+  L.n_tiles = reinterpret_cast<int32_t*>(ws + off);
+  L.max_tiles = mt;
+  return launched(e4b::launch_int4_gemv(L, (hipStream_t)stream));
+}
 
 int e4b_version(void) { return 300; }
 

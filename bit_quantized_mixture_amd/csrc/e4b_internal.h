@@ -86,6 +86,32 @@ struct DgradLaunch {
 hipError_t launch_dgrad(const DgradLaunch& L, hipStream_t stream);
 int dgrad_tile_rows();
 
+// int4-b32: packer, per-token int8 activations (xs == nullptr: natural order, no block sums;
+// otherwise the GEMV's permuted order plus block sums), and the routed decode GEMV.
+hipError_t launch_pack_int4(const uint16_t* w, int64_t n_elems, uint8_t* packed, uint16_t* scales,
+                            hipStream_t stream);
+hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t K, int8_t* q, float* s,
+                            int32_t* xs, hipStream_t stream);
+struct Int4GemvLaunch {
+  int64_t E, N, K, T;
+  int k;
+  const uint16_t* x;
+  const uint8_t* wq;
+  const uint16_t* sc;
+  const int32_t* offsets;
+  const int32_t* slots;
+  float* out;
+  int8_t* qx;          // workspace [T, K]
+  int32_t* xs;         // workspace [T, K/32]
+  float* sx;           // workspace [T]
+  int32_t* tiles;      // workspace [max_tiles, 4]
+  int32_t* n_tiles;    // workspace [2]
+  int64_t max_tiles;
+};
+hipError_t launch_int4_gemv(const Int4GemvLaunch& L, hipStream_t stream);
+int int4_gemv_tile_rows(int64_t T);
+size_t int4_gemv_lds_bytes(int64_t T, int64_t K);
+
 // Small-M streaming kernels: stage 0 = gate_up + SwiGLU (x16 -> h), 1 = down (h -> y).
 hipError_t launch_gemv(const MoeLaunch& L, hipStream_t stream, int stage);
 // The same kernels over the tail tiles of the MFMA-tile path (its activation order).

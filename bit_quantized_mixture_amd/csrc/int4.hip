@@ -1,0 +1,328 @@
+// int4-b32 decode GEMV over routed experts with exact integer accumulation, its round-to-nearest
+// packer and the per-token int8 activation quantiser.
+//
+// grouped-nf4-gemm 0.25.0 project description, opening section: the package carries an int4-b32
+// decode GEMV and a packer for it.  Cerin Amroth "ML systems" index, Solutions: a single-token
+// int4-b32 decode GEMV over routed MoE experts with exact integer accumulation.  The pages fix
+// nothing else; the format read here: signed 4-bit codes (two's complement, even element in the
+// low nibble), one fp16 scale s = fp16(absmax / 7) per 32 weights of a row; activations
+// quantised per token to int8 with s_x = absmax / 127; y[n] = s_x * sum_b s[n, b] * I_b with
+// I_b the exact int32 dot product of block b's codes and the token's int8 codes.
+//
+// GEMV layout: a workgroup of 8 waves owns one tile of <= 16 routed rows of one expert (their
+// tokens' int8 rows staged in LDS) and 128 / ksplit weight rows; the K axis is cut into ksplit
+// parts, one per wave of a row group, summed through LDS at the end in a fixed order.  Lane
+// (r, g) of a wave streams 16 contiguous bytes (one 32-weight block) of row r at block 4c + g
+// of chunk c, so a wave's load covers 64 contiguous bytes of each of 16 rows.  Codes are read
+// as u = q + 8 (the nibble XOR 8, 0..15) so a byte-wise mask gives the dot-product operand;
+// the block sum of the token's codes times 8 is subtracted back (exact):
+//   I_b = sum u * x - 8 * sum x.
+// The activation rows are stored with each group of 8 elements in the order 0,2,4,6,1,3,5,7,
+// the order of the low and high nibbles of a packed dword, so v_dot4 pairs the right elements.
+#include "e4b_device.h"
+#include "e4b_internal.h"
+
+namespace e4b {
+
+namespace {
+
+constexpr int kI4Block = 32;
+constexpr int kGvWaves = 8;
+constexpr int kGvTok = 16;  // routed rows per tile
+
+// ---- packer: lane per 8 weights (one 16-byte load), 4 lanes per block.
+__global__ void __launch_bounds__(256) pack_int4_kernel(const uint16_t* __restrict__ w,
+                                                        uint8_t* __restrict__ packed,
+                                                        uint16_t* __restrict__ scales,
+                                                        int64_t n_chunks) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  // n_chunks and the stride are multiples of 4, so the 4 lanes of a block stay together
+  for (int64_t q = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; q < n_chunks; q += stride) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(w + 8 * q);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(raw[i] << 16);
+      v[2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
+    }
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+    a = fmaxf(a, __shfl_xor(a, 1, 4));
+    a = fmaxf(a, __shfl_xor(a, 2, 4));
+    const _Float16 s16 = (_Float16)__fdiv_rn(a, 7.0f);  // correctly rounded, then RNE to fp16
+    const float s = (float)s16;
+    uint32_t word = 0;
+    if (s > 0.f) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float r = fminf(fmaxf(rintf(__fdiv_rn(v[i], s)), -8.f), 7.f);
+        word |= (uint32_t(int(r)) & 0xFu) << (4 * i);  // element 2p: low nibble of byte p
+      }
+    }
+    reinterpret_cast<uint32_t*>(packed)[q] = word;
+    if ((q & 3) == 0) scales[q >> 2] = __builtin_bit_cast(uint16_t, s16);
+  }
+}
+
+// ---- activation quantiser: one workgroup per token.  PERM stores each group of 8 codes in
+// the order 0,2,4,6,1,3,5,7 and writes the block sums of the codes.
+template <bool PERM>
+__global__ void __launch_bounds__(256) quant_act_kernel(const uint16_t* __restrict__ x, int64_t K,
+                                                        int8_t* __restrict__ q,
+                                                        float* __restrict__ s_out,
+                                                        int32_t* __restrict__ xs) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x;
+  const int64_t t = blockIdx.x;
+  const uint16_t* xr = x + t * K;
+  const int ngroups = int(K >> 3);
+  float a = 0.f;
+  for (int g = tid; g < ngroups; g += 256) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(xr + 8 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a = fmaxf(a, fmaxf(fabsf(__uint_as_float(raw[i] << 16)),
+                         fabsf(__uint_as_float(raw[i] & 0xFFFF0000u))));
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) a = fmaxf(a, __shfl_xor(a, m));
+  if ((tid & 63) == 0) red[tid >> 6] = a;
+  __syncthreads();
+  a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = __fdiv_rn(a, 127.0f);
+  if (tid == 0) s_out[t] = s;
+  // ngroups is a multiple of 4 and the stride 256, so the 4 lanes of a block stay together
+  for (int g = tid; g < ngroups; g += 256) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(xr + 8 * g);
+    int c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float v = __uint_as_float(i & 1 ? raw[i >> 1] & 0xFFFF0000u : raw[i >> 1] << 16);
+      const float r = s > 0.f ? fminf(fmaxf(rintf(__fdiv_rn(v, s)), -127.f), 127.f) : 0.f;
+      c[i] = int(r);
+    }
+    uint32_t lo, hi;
+    if (PERM) {
+      lo = (c[0] & 0xFF) | ((c[2] & 0xFF) << 8) | ((c[4] & 0xFF) << 16) | (uint32_t(c[6] & 0xFF) << 24);
+      hi = (c[1] & 0xFF) | ((c[3] & 0xFF) << 8) | ((c[5] & 0xFF) << 16) | (uint32_t(c[7] & 0xFF) << 24);
+    } else {
+      lo = (c[0] & 0xFF) | ((c[1] & 0xFF) << 8) | ((c[2] & 0xFF) << 16) | (uint32_t(c[3] & 0xFF) << 24);
+      hi = (c[4] & 0xFF) | ((c[5] & 0xFF) << 8) | ((c[6] & 0xFF) << 16) | (uint32_t(c[7] & 0xFF) << 24);
+    }
+    *reinterpret_cast<u32x2*>(q + t * K + 8 * g) = u32x2{lo, hi};
+    if (PERM) {
+      int sum = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sum += c[i];
+      sum += __shfl_xor(sum, 1, 4);
+      sum += __shfl_xor(sum, 2, 4);
+      if ((g & 3) == 0) xs[t * (K >> 5) + (g >> 2)] = sum;
+    }
+  }
+}
+
+struct I4Args {
+  const uint8_t* wq;        // [E, N, K/2]
+  const uint16_t* sc;       // [E, N, K/32] fp16 bits
+  const int8_t* qx;         // [T, K] int8, permuted groups
+  const int32_t* xs;        // [T, K/32] block sums of qx
+  const float* sx;          // [T]
+  const int32_t* slots;     // [S] sorted slots
+  const int32_t* tiles;     // [max_tiles, 4]: expert, first sorted row, rows, 0
+  const int32_t* n_tiles;
+  float* out;               // [S, N] float32, sorted rows
+  int64_t N, K;
+  int32_t k, n_rblocks, tile_rows, ksplit;
+};
+
+__global__ void __launch_bounds__(512) int4_gemv_kernel(I4Args p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rb = int(blockIdx.x) % p.n_rblocks;
+  const int it = int(blockIdx.x) / p.n_rblocks;
+  if (it >= *p.n_tiles) return;  // uniform
+  const int e = p.tiles[4 * it], row0 = p.tiles[4 * it + 1], ntok = p.tiles[4 * it + 2];
+  const int64_t K = p.K;
+  const int nb = int(K >> 5);  // blocks per row
+  const int ks = p.ksplit, rows_wg = 16 * (kGvWaves / ks);
+  int8_t* act = reinterpret_cast<int8_t*>(lds);                                // [tile_rows][K]
+  int32_t* xsl = reinterpret_cast<int32_t*>(lds + int64_t(p.tile_rows) * K);   // [tile_rows][nb]
+  float* part = reinterpret_cast<float*>(lds + int64_t(p.tile_rows) * K + int64_t(p.tile_rows) * nb * 4);
+
+  // stage the tile's token rows (int8 codes and block sums)
+  const int pieces = int(K >> 4);
+  for (int i = tid; i < ntok * pieces; i += 512) {
+    const int tt = i / pieces, c = i - tt * pieces;
+    const int64_t tok = p.slots[row0 + tt] / p.k;
+    *reinterpret_cast<u32x4*>(act + tt * K + 16 * c) =
+        *reinterpret_cast<const u32x4*>(p.qx + tok * K + 16 * c);
+  }
+  for (int i = tid; i < ntok * nb; i += 512) {
+    const int tt = i / nb, b = i - tt * nb;
+    const int64_t tok = p.slots[row0 + tt] / p.k;
+    xsl[tt * nb + b] = p.xs[tok * nb + b];
+  }
+  __syncthreads();
+
+  const int kq = wave % ks, rg = wave / ks;
+  const int r = lane >> 2, g = lane & 3;
+  const int rl = 16 * rg + r;                       // row inside the workgroup's block
+  const int64_t n = int64_t(rb) * rows_wg + rl;
+  const int nch = int(K >> 7);                      // 128-weight chunks per row
+  const int c0 = (kq * nch) / ks, c1 = ((kq + 1) * nch) / ks;
+  const uint32_t kb = uint32_t(K >> 1);
+  const __amdgpu_buffer_rsrc_t wres =
+      buffer_rsrc(p.wq + int64_t(e) * p.N * kb, uint32_t(p.N * kb));
+  const __amdgpu_buffer_rsrc_t sres =
+      buffer_rsrc(p.sc + int64_t(e) * p.N * nb, uint32_t(p.N * nb * 2));
+  const uint32_t woff = uint32_t(n) * kb + 16u * g;
+  const uint32_t soff = (uint32_t(n) * uint32_t(nb) + g) * 2u;
+
+  float acc[kGvTok];
+#pragma unroll
+  for (int tt = 0; tt < kGvTok; ++tt) acc[tt] = 0.f;
+
+  // Chunks in groups of 4 with the next group's loads in flight (two register sets); loads
+  // past the wave's last chunk repeat it (in bounds, never used).
+  u32x4 wA[4], wB[4];
+  uint32_t sA[4], sB[4];
+  auto load4 = [&](int cb, u32x4 (&w)[4], uint32_t (&s)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = cb + j < c1 ? cb + j : c1 - 1;
+      w[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, woff, 64u * c, 0));
+      s[j] = __builtin_amdgcn_raw_buffer_load_b16(sres, soff, 8u * c, 0);
+    }
+  };
+  auto compute = [&](const u32x4& wv, uint32_t sv, int c) {
+    const int b = 4 * c + g;
+    const float sf = float(__builtin_bit_cast(_Float16, uint16_t(sv)));
+    uint32_t u[8];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      u[2 * d] = (wv[d] & 0x0F0F0F0Fu) ^ 0x08080808u;
+      u[2 * d + 1] = ((wv[d] >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
+    }
+    const int8_t* ab = act + 32 * b;
+#pragma unroll
+    for (int tt = 0; tt < kGvTok; ++tt) {
+      if (tt < ntok) {  // uniform
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(ab + tt * K);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(ab + tt * K + 16);
+        int isum = -8 * xsl[tt * nb + b];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) isum = __builtin_amdgcn_sdot4(int(u[i]), int(a0[i]), isum, false);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) isum = __builtin_amdgcn_sdot4(int(u[4 + i]), int(a1[i]), isum, false);
+        acc[tt] = fmaf(sf, float(isum), acc[tt]);
+      }
+    }
+  };
+  if (c0 < c1) {  // uniform
+    load4(c0, wA, sA);
+    for (int c = c0; c < c1; c += 8) {
+      load4(c + 4, wB, sB);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (c + j < c1) compute(wA[j], sA[j], c + j);
+      load4(c + 8, wA, sA);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (c + 4 + j < c1) compute(wB[j], sB[j], c + 4 + j);
+    }
+  }
+  // the 4 block lanes of a row, then the ksplit waves of a row group through LDS
+#pragma unroll
+  for (int tt = 0; tt < kGvTok; ++tt) {
+    acc[tt] += __shfl_xor(acc[tt], 1);
+    acc[tt] += __shfl_xor(acc[tt], 2);
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int tt = 0; tt < kGvTok; ++tt)
+      if (tt < ntok) part[(rl * ks + kq) * kGvTok + tt] = acc[tt];
+  }
+  __syncthreads();
+  for (int i = tid; i < rows_wg * ntok; i += 512) {
+    const int tt = i / rows_wg, row = i - tt * rows_wg;
+    float sum = 0.f;
+    for (int q = 0; q < ks; ++q) sum += part[(row * ks + q) * kGvTok + tt];
+    const int64_t tok = p.slots[row0 + tt] / p.k;
+    p.out[int64_t(row0 + tt) * p.N + int64_t(rb) * rows_wg + row] = sum * p.sx[tok];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack_int4(const uint16_t* w, int64_t n_elems, uint8_t* packed, uint16_t* scales,
+                            hipStream_t stream) {
+  const int64_t n_chunks = n_elems / 8;
+  const int64_t want = (n_chunks + 255) / 256;
+  const unsigned grid = unsigned(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(pack_int4_kernel, dim3(grid), dim3(256), 0, stream, w, packed, scales, n_chunks);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t K, int8_t* q, float* s,
+                            int32_t* xs, hipStream_t stream) {
+  if (xs)
+    hipLaunchKernelGGL(quant_act_kernel<true>, dim3(unsigned(T)), dim3(256), 0, stream, x, K, q, s, xs);
+  else
+    hipLaunchKernelGGL(quant_act_kernel<false>, dim3(unsigned(T)), dim3(256), 0, stream, x, K, q, s, xs);
+  return hipGetLastError();
+}
+
+int int4_gemv_tile_rows(int64_t T) { return int(T < kGvTok ? T : kGvTok); }
+
+int int4_gemv_ksplit(int64_t max_tiles, int64_t N, int64_t K) {
+  // the smallest split that gives every CU several waves, with >= 2 chunks per wave and
+  // whole row blocks
+  for (int ks = 1; ks <= 8; ks <<= 1) {
+    const int64_t rows_wg = 16 * (kGvWaves / ks);
+    if (N % rows_wg) continue;
+    const int64_t waves = max_tiles * (N / rows_wg) * kGvWaves;
+    if (waves >= 8192 || ks == 8 || (K >> 7) < 4 * ks) return ks;
+  }
+  return 8;
+}
+
+size_t int4_gemv_lds_bytes(int64_t T, int64_t K) {
+  const int64_t tr = int4_gemv_tile_rows(T);
+  return size_t(tr * K + tr * (K >> 5) * 4 + 128 * kGvTok * 4);
+}
+
+hipError_t launch_int4_gemv(const Int4GemvLaunch& L, hipStream_t stream) {
+  hipError_t err = launch_quant_act(L.x, L.T, L.K, L.qx, L.sx, L.xs, stream);
+  if (err != hipSuccess) return err;
+  const int tr = int4_gemv_tile_rows(L.T);
+  err = launch_build_tiles(L.offsets, int(L.E), tr, L.tiles, L.n_tiles, stream);
+  if (err != hipSuccess) return err;
+  I4Args a{};
+  a.wq = L.wq;
+  a.sc = L.sc;
+  a.qx = L.qx;
+  a.xs = L.xs;
+  a.sx = L.sx;
+  a.slots = L.slots;
+  a.tiles = L.tiles;
+  a.n_tiles = L.n_tiles;
+  a.out = L.out;
+  a.N = L.N;
+  a.K = L.K;
+  a.k = L.k;
+  a.ksplit = int4_gemv_ksplit(L.max_tiles, L.N, L.K);
+  a.n_rblocks = int(L.N / (16 * (kGvWaves / a.ksplit)));
+  a.tile_rows = tr;
+  const size_t lds = int4_gemv_lds_bytes(L.T, L.K);
+  if (lds > 64 * 1024) {
+    err = hipFuncSetAttribute(reinterpret_cast<const void*>(int4_gemv_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (err != hipSuccess) return err;
+  }
+  const unsigned grid = unsigned(L.max_tiles * a.n_rblocks);
+  hipLaunchKernelGGL(int4_gemv_kernel, dim3(grid), dim3(512), lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace e4b

@@ -210,6 +210,65 @@ int e4b_dgrad_workspace_bytes(const e4b_dgrad_args* a, size_t* bytes);
  */
 int e4b_grouped_dgrad(const e4b_dgrad_args* a, void* stream);
 
+/*
+ * e4b_pack_int4_b32 — round-to-nearest int4-b32 packing of bf16 stacks (grouped-nf4-gemm
+ * 0.25.0 project description, opening section: the int4-b32 decode GEMV and its packer; the
+ * pages give no conversion rule, the one below is the plain round-to-nearest reading; the
+ * calibrated GPTQ packer needs calibration data and is not provided).
+ *   w       [E, N, K] bf16 bits.  K % 32 == 0.
+ *   packed  [E, N, K/2] uint8 out: signed 4-bit codes q in [-8, 7], two's complement; byte p
+ *           of a row holds element 2p in the low nibble and 2p+1 in the high nibble.
+ *   scales  [E, N, K/32] fp16 bits out: s = fp16(absmax / 7) of each 32-block (float32
+ *           division, correctly rounded, then round-to-nearest-even to fp16).
+ * q = clamp(rint(w / s), -8, 7) with the float32 division by the stored scale; an all-zero
+ * block (or one whose scale rounds to 0) gets s = 0 and q = 0.  Weight = s * q.  Bit-exact.
+ */
+int e4b_pack_int4_b32(const uint16_t* w, int64_t E, int64_t N, int64_t K,
+                      uint8_t* packed, uint16_t* scales, void* stream);
+
+/*
+ * e4b_quantize_act_int8 — the per-token int8 activations the int4-b32 GEMV multiplies
+ * (exact integer accumulation needs integer activations; the pages give no rule, one
+ * float32 scale per token is taken).
+ *   x   [T, K] bf16 bits.  K % 32 == 0.
+ *   q   [T, K] int8 out: clamp(rint(x / s), -127, 127) (float32 division, correctly rounded).
+ *   s   [T] float32 out: absmax of the row / 127 (correctly rounded); an all-zero row gets s = 0
+ *       and q = 0.  Bit-exact.
+ */
+int e4b_quantize_act_int8(const uint16_t* x, int64_t T, int64_t K, int8_t* q, float* s,
+                          void* stream);
+
+/* Arguments of e4b_gemv_int4_b32. */
+typedef struct e4b_int4_gemv_args {
+  int64_t E, N, K;        /* int4-b32 stack [E, N, K]; N % 16 == 0, K % 128 == 0, K <= 8192 */
+  int64_t T;              /* tokens */
+  int32_t k;              /* routed experts per token: 1 <= k <= E, k <= 64 */
+  int32_t reserved;       /* must be 0 */
+  const uint16_t* x;      /* [T, K] bf16 bits */
+  const uint8_t* w;       /* [E, N, K/2] as packed by e4b_pack_int4_b32 */
+  const uint16_t* s;      /* [E, N, K/32] fp16 bits */
+  const int32_t* expert_offsets; /* [E+1], from e4b_route_permute */
+  const int32_t* sorted_slots;   /* [T*k], from e4b_route_permute */
+  float* out_f32;         /* [T*k, N] float32 out, rows in sorted order */
+  void* ws;               /* device workspace of at least e4b_int4_gemv_workspace_bytes() */
+  size_t ws_bytes;
+} e4b_int4_gemv_args;
+
+/* Workspace bytes e4b_gemv_int4_b32 needs for the sizes in `a`. */
+int e4b_int4_gemv_workspace_bytes(const e4b_int4_gemv_args* a, size_t* bytes);
+
+/*
+ * e4b_gemv_int4_b32 — the routed decode GEMV on int4-b32 weights with exact integer
+ * accumulation (Cerin Amroth "ML systems" index, Solutions: a single-token int4 decode GEMV
+ * over routed MoE experts).  For every sorted row p of expert e (token t = sorted_slots[p] / k):
+ *   out_f32[p, n] = s_x[t] * sum_b s[e, n, b] * I_b,
+ * I_b = sum over the 32 k of block b of q[e, n, k] * q_x[t, k], an exact int32 sum, with q_x,
+ * s_x the activations of e4b_quantize_act_int8 (recomputed inside, in the workspace).  The
+ * block terms are summed in float32 in a fixed order: deterministic.  A dense layer is the
+ * case E = 1, k = 1.  Synchronous errors as e4b_moe_forward.
+ */
+int e4b_gemv_int4_b32(const e4b_int4_gemv_args* a, void* stream);
+
 /* Static description of a status code. */
 const char* e4b_status_string(int status);
 

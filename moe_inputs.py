@@ -31,7 +31,7 @@ TID_X, TID_LOGITS, TID_GATE_UP, TID_DOWN, TID_B_GU, TID_B_DN = 0, 1, 2, 3, 4, 5
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    fmt: str          # "nf4" or "mxfp4"
+    fmt: str          # "nf4", "mxfp4" or "int4" (int4-b32)
     E: int
     H: int
     I: int
@@ -63,6 +63,14 @@ WORKLOADS = {
                                    zipf_s=1.2),
 }
 DECODE_TOKENS = (1, 4, 16, 64)
+
+# Stacks for the int4-b32 decode GEMV (gate_up-shaped, N = 2I, K = H): the fine-grained decode
+# layer's experts, and one dense [14336, 4096] matrix at M = 1 (one expert, every token routed
+# to it).
+INT4_WORKLOADS = {
+    "finegrained_int4_decode": Workload("finegrained_int4_decode", "int4", E=128, H=2048, I=768, k=8, T=64),
+    "dense_int4_decode": Workload("dense_int4_decode", "int4", E=1, H=4096, I=7168, k=1, T=1),
+}
 
 
 def _rng(seed: int, tid: int, e: int = 0) -> np.random.Generator:

@@ -23,7 +23,8 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("e4b_pack_nf4", "e4b_pack_mxfp4", "e4b_route_permute", "e4b_moe_forward",
               "e4b_route_workspace_bytes", "e4b_moe_workspace_bytes", "e4b_status_string", "e4b_version",
-              "e4b_dgrad_workspace_bytes", "e4b_grouped_dgrad"):
+              "e4b_dgrad_workspace_bytes", "e4b_grouped_dgrad", "e4b_pack_int4_b32",
+              "e4b_quantize_act_int8", "e4b_int4_gemv_workspace_bytes", "e4b_gemv_int4_b32"):
         assert n in names
 
 
@@ -152,3 +153,39 @@ def test_dgrad_rejects_bad_arguments(e4b):
     assert f(ws_bytes=16) == ERR_WORKSPACE
     assert f(S=1 << 24, N=1 << 10) == ERR_OVERFLOW
     assert e4b.e4b_dgrad_workspace_bytes("nf4", 4, 128, 256, 100) >= 64
+
+
+def test_int4_entry_points_reject_bad_arguments(e4b):
+    pk = lambda w=FAKE, E=2, N=4, K=64, o1=FAKE, o2=FAKE: e4b._c_pack_int4(w, E, N, K, o1, o2, None)
+    assert pk(w=None) == ERR_ARG
+    assert pk(E=0) == ERR_ARG
+    assert pk(K=48) == ERR_SHAPE
+    assert pk(o2=FAKE + 2) == ERR_ALIGN
+    qa = lambda x=FAKE, T=3, K=64, q=FAKE, s=FAKE: e4b._c_quant_act(x, T, K, q, s, None)
+    assert qa(q=None) == ERR_ARG
+    assert qa(T=-1) == ERR_ARG
+    assert qa(K=40) == ERR_SHAPE
+    assert qa(x=FAKE + 8) == ERR_ALIGN
+
+    def f(**kw):
+        a = e4b._int4_args(8, 256, 1024, 4, 2)
+        for n in ("x", "w", "s", "expert_offsets", "sorted_slots", "out_f32", "ws"):
+            setattr(a, n, FAKE)
+        a.ws_bytes = 1 << 40
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return e4b._c_int4_gemv(ctypes.byref(a), None)
+    assert f(E=0) == ERR_ARG
+    assert f(k=0) == ERR_ARG
+    assert f(k=9) == ERR_ARG
+    assert f(T=-1) == ERR_ARG
+    assert f(reserved=1) == ERR_ARG
+    assert f(N=250) == ERR_SHAPE
+    assert f(K=1000) == ERR_SHAPE
+    assert f(K=8320) == ERR_SHAPE
+    assert f(x=None) == ERR_ARG
+    assert f(sorted_slots=FAKE + 4) == ERR_ALIGN
+    assert f(ws_bytes=64) == ERR_WORKSPACE
+    assert f(N=1 << 20, K=8192) == ERR_OVERFLOW
+    n = e4b.e4b_int4_gemv_workspace_bytes(8, 256, 1024, 4, 2)
+    assert n >= 4 * 1024 + 4 * 32 * 4 + 4 * 4
