@@ -14,7 +14,9 @@ GLU, per-expert biases) and the 128-expert decode layer at T = 64, 16, 4, 1 (war
 256 MB Infinity Cache flushed by reading 1 GiB before every step; eager launches with per-stage HIP events,
 and the same step replayed from a HIP graph), and a float64 CPU-oracle baseline timed on a
 bounded sample of the headline workload.  Also under "secondary": the grouped dgrad on the
-headline layer's packed down and gate_up stacks with its own routing.
+headline layer's packed down and gate_up stacks with its own routing, and the int4-b32 routed
+decode GEMV (exact integer accumulation) on the decode layer's gate_up stack at T = 64 and 1
+and on one dense [14336, 4096] matrix at M = 1, in GB/s of weight streaming.
 """
 from __future__ import annotations
 
@@ -31,7 +33,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from moe_inputs import WORKLOADS, make_bias, make_expert_weight, make_logits, make_x  # noqa: E402
+from moe_inputs import INT4_WORKLOADS, WORKLOADS, make_bias, make_expert_weight, make_logits, make_x  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, AMD published
 PEAK_F16_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, AMD published
@@ -368,6 +370,48 @@ def dgrad_report(torch, layer: Layer, steps: int, warmup: int) -> dict:
     return rep
 
 
+def int4_report(torch, e4b, wl, T: int, steps: int, warmup: int) -> dict:
+    """The int4-b32 routed decode GEMV on the workload's gate_up-shaped stack (seeded bf16
+    weights packed on the GPU by e4b_pack_int4_b32), T tokens routed by the seeded logits.
+    One call = activation quantiser + tile list + GEMV, timed with HIP events on the current
+    stream.  Algorithmic bytes: the active experts' codes and scales (0.5625 B per weight),
+    x (2 B per element) and the fp32 output."""
+    dev = "cuda:0"
+    N, K = 2 * wl.I, wl.H
+    w = torch.empty((wl.E, N, K), dtype=torch.bfloat16, device=dev)
+    for e in range(wl.E):
+        w[e].copy_(torch.from_numpy(make_expert_weight(wl, "gate_up", e).view(np.int16)).view(torch.bfloat16))
+    packed, scales = e4b.e4b_pack_int4_b32(w)
+    del w
+    wt = wl.with_T(T)
+    x = torch.from_numpy(make_x(wt).view(np.int16)).to(dev).view(torch.bfloat16)
+    _, _, off, slots = e4b.e4b_route_permute(torch.from_numpy(make_logits(wt)).to(dev), wl.k)
+    out = torch.empty((T * wl.k, N), dtype=torch.float32, device=dev)
+    ws = torch.empty((max(e4b.e4b_int4_gemv_workspace_bytes(wl.E, N, K, T, wl.k), 256),),
+                     dtype=torch.uint8, device=dev)
+    run = lambda: e4b.e4b_gemv_int4_b32(packed, scales, x, wl.k, off, slots, out=out, ws=ws)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    active = int((torch.diff(off) > 0).sum().item())
+    gc.collect()
+    gc.disable()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        run()
+    t1.record()
+    torch.cuda.synchronize()
+    gc.enable()
+    ms = t0.elapsed_time(t1) / steps
+    nbytes = active * N * K * 0.5625 + T * K * 2 + T * wl.k * N * 4
+    gbs = nbytes / (ms / 1e3) / 1e9
+    del packed, scales, x, out, ws
+    torch.cuda.empty_cache()
+    return {"ms": ms, "T": T, "E": wl.E, "N": N, "K": K, "k": wl.k, "active_experts": active,
+            "algorithmic_bytes": nbytes, "achieved_gbs": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS}
+
+
 def fmt_rep(key, rep):
     rl = rep["roofline"]
     s = (f"[bench] {key}: {rep['ms_per_step']:.4f} ms/step, {rep['tokens_per_s']:.0f} tok/s, "
@@ -384,13 +428,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_nf4_prefill", choices=list(WORKLOADS))
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--secondary", default="all",
+                    help="comma list of secondary sections to run: dgrad, prefill (the skewed and "
+                         "MXFP4 layers), int4, decode; default all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flags", type=lambda v: int(v, 0), default=0,
                     help="e4b_moe_args.flags for the headline workload (path / tile override)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the layer runs on a "
-              "single MI355X here; see the sharding notes in the design document.", file=sys.stderr)
+              "single MI355X; the multi-GPU (expert- or tensor-parallel) path is not built.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -406,14 +453,16 @@ def main():
     main_rep = batch_report(torch, layer, wl.T, args.steps, args.warmup, flags=args.flags)
     log(fmt_rep(wl.name, main_rep) + f"; stages {main_rep['stage_ms']}")
     secondary = {}
-    if not args.no_secondary:
+    sections = set() if args.no_secondary else (
+        {"dgrad", "prefill", "int4", "decode"} if args.secondary == "all" else set(args.secondary.split(",")))
+    if "dgrad" in sections:
         secondary[wl.name + "_dgrad"] = dg = dgrad_report(torch, layer, max(args.steps, 10), args.warmup)
         log(f"[bench] {wl.name} dgrad: " + ", ".join(
             f"{k} {v['ms']:.3f} ms {v['tflops']:.1f} TFLOP/s ({100 * v['frac_of_mfma_peak']:.1f}%)" for k, v in dg.items()))
     del layer
     torch.cuda.empty_cache()
 
-    if not args.no_secondary:
+    if "prefill" in sections:
         for name in ("skewed_nf4_prefill", "mxfp4_moe"):
             if name == wl.name:
                 continue
@@ -433,6 +482,14 @@ def main():
                 log(fmt_rep(key, secondary[key]))
             del lay
             torch.cuda.empty_cache()
+    if "int4" in sections:
+        for name, T in (("finegrained_int4_decode", 64), ("finegrained_int4_decode", 1),
+                        ("dense_int4_decode", 1)):
+            key = f"{name}_T{T}"
+            secondary[key] = r = int4_report(torch, e4b, INT4_WORKLOADS[name], T, max(args.steps, 50), args.warmup)
+            log(f"[bench] {key}: {r['ms'] * 1e3:.2f} us/call, {r['achieved_gbs']:.1f} GB/s "
+                f"({100 * r['frac_of_hbm_peak']:.1f}% of HBM peak), {r['active_experts']} experts")
+    if "decode" in sections:
         dwl = WORKLOADS["finegrained_nf4_decode"]
         lay = Layer(e4b, torch, dwl)
         for T, flush in ((64, 0), (16, 0), (4, 0), (1, 0), (64, MALL_FLUSH_BYTES), (1, MALL_FLUSH_BYTES)):

@@ -150,21 +150,6 @@ __global__ void __launch_bounds__(512) int4_gemv_kernel(I4Args p) {
   int32_t* xsl = reinterpret_cast<int32_t*>(lds + int64_t(p.tile_rows) * K);   // [tile_rows][nb]
   float* part = reinterpret_cast<float*>(lds + int64_t(p.tile_rows) * K + int64_t(p.tile_rows) * nb * 4);
 
-  // stage the tile's token rows (int8 codes and block sums)
-  const int pieces = int(K >> 4);
-  for (int i = tid; i < ntok * pieces; i += 512) {
-    const int tt = i / pieces, c = i - tt * pieces;
-    const int64_t tok = p.slots[row0 + tt] / p.k;
-    *reinterpret_cast<u32x4*>(act + tt * K + 16 * c) =
-        *reinterpret_cast<const u32x4*>(p.qx + tok * K + 16 * c);
-  }
-  for (int i = tid; i < ntok * nb; i += 512) {
-    const int tt = i / nb, b = i - tt * nb;
-    const int64_t tok = p.slots[row0 + tt] / p.k;
-    xsl[tt * nb + b] = p.xs[tok * nb + b];
-  }
-  __syncthreads();
-
   const int kq = wave % ks, rg = wave / ks;
   const int r = lane >> 2, g = lane & 3;
   const int rl = 16 * rg + r;                       // row inside the workgroup's block
@@ -219,8 +204,24 @@ __global__ void __launch_bounds__(512) int4_gemv_kernel(I4Args p) {
       }
     }
   };
+  // the first weight loads go out before the activations are staged, so the two latencies
+  // overlap
+  if (c0 < c1) load4(c0, wA, sA);  // uniform
+  // stage the tile's token rows (int8 codes and block sums)
+  const int pieces = int(K >> 4);
+  for (int i = tid; i < ntok * pieces; i += 512) {
+    const int tt = i / pieces, c = i - tt * pieces;
+    const int64_t tok = p.slots[row0 + tt] / p.k;
+    *reinterpret_cast<u32x4*>(act + tt * K + 16 * c) =
+        *reinterpret_cast<const u32x4*>(p.qx + tok * K + 16 * c);
+  }
+  for (int i = tid; i < ntok * nb; i += 512) {
+    const int tt = i / nb, b = i - tt * nb;
+    const int64_t tok = p.slots[row0 + tt] / p.k;
+    xsl[tt * nb + b] = p.xs[tok * nb + b];
+  }
+  __syncthreads();
   if (c0 < c1) {  // uniform
-    load4(c0, wA, sA);
     for (int c = c0; c < c1; c += 8) {
       load4(c + 4, wB, sB);
 #pragma unroll
