@@ -152,6 +152,7 @@ int int4_check(const e4b_int4_gemv_args* a, int64_t* max_tiles) {
   const int64_t bm = a->T > 0 ? e4b::int4_gemv_tile_rows(a->T) : 1;
   const int64_t active = a->E < S ? a->E : S;
   *max_tiles = (S + active * (bm - 1)) / bm;
+  if (*max_tiles * (a->N / 16) >= (int64_t(1) << 31)) return E4B_ERR_OVERFLOW;  // grid size
   return E4B_OK;
 }
 
@@ -232,7 +233,7 @@ int e4b_gemv_int4_b32(const e4b_int4_gemv_args* a, void* stream) {
   return launched(e4b::launch_int4_gemv(L, (hipStream_t)stream));
 }
 
-int e4b_version(void) { return 300; }
+int e4b_version(void) { return 400; }
 
 
 int e4b_dgrad_workspace_bytes(const e4b_dgrad_args* a, size_t* bytes) {
