@@ -277,13 +277,13 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t K, int8_t* q, 
 int int4_gemv_tile_rows(int64_t T) { return int(T < kGvTok ? T : kGvTok); }
 
 int int4_gemv_ksplit(int64_t max_tiles, int64_t N, int64_t K) {
-  // the smallest split that gives every CU several waves, with >= 2 chunks per wave and
-  // whole row blocks
+  // The smallest K split (with whole row blocks) that gives the chip >= 8192 waves, short of
+  // a split that would leave a wave fewer than 4 chunks of 128 weights.
   for (int ks = 1; ks <= 8; ks <<= 1) {
     const int64_t rows_wg = 16 * (kGvWaves / ks);
     if (N % rows_wg) continue;
     const int64_t waves = max_tiles * (N / rows_wg) * kGvWaves;
-    if (waves >= 8192 || ks == 8 || (K >> 7) < 4 * ks) return ks;
+    if (waves >= 8192 || ks == 8 || (K >> 7) < 4 * 2 * ks) return ks;
   }
   return 8;
 }
