@@ -179,7 +179,7 @@ int e4b_quantize_act_int8(const uint16_t* x, int64_t T, int64_t K, int8_t* q, fl
   if (T >= (int64_t(1) << 31) || K >= (int64_t(1) << 31)) return E4B_ERR_OVERFLOW;
   const int st = check_device();
   if (st != E4B_OK || T == 0) return st;
-  return launched(e4b::launch_quant_act(x, T, K, q, s, nullptr, (hipStream_t)stream));
+  return launched(e4b::launch_quant_act(x, T, K, q, s, (hipStream_t)stream));
 }
 
 int e4b_int4_gemv_workspace_bytes(const e4b_int4_gemv_args* a, size_t* bytes) {

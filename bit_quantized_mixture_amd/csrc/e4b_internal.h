@@ -86,12 +86,12 @@ struct DgradLaunch {
 hipError_t launch_dgrad(const DgradLaunch& L, hipStream_t stream);
 int dgrad_tile_rows();
 
-// int4-b32: packer, per-token int8 activations (xs == nullptr: natural order, no block sums;
-// otherwise the GEMV's permuted order plus block sums), and the routed decode GEMV.
+// int4-b32: packer, per-token int8 activations in natural order, and the routed decode GEMV
+// (which quantises into its own permuted layout).
 hipError_t launch_pack_int4(const uint16_t* w, int64_t n_elems, uint8_t* packed, uint16_t* scales,
                             hipStream_t stream);
 hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t K, int8_t* q, float* s,
-                            int32_t* xs, hipStream_t stream);
+                            hipStream_t stream);
 struct Int4GemvLaunch {
   int64_t E, N, K, T;
   int k;

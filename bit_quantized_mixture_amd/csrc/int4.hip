@@ -65,16 +65,60 @@ __global__ void __launch_bounds__(256) pack_int4_kernel(const uint16_t* __restri
   }
 }
 
+// Tile list for the GEMV (run by one extra workgroup of the quantiser launch): for each expert
+// e, tiles of <= bm consecutive sorted rows: (e, first row, rows, 0), experts in order; the
+// count goes to n_tiles[0].
+__device__ void int4_build_tiles(const int32_t* __restrict__ offsets, int E, int bm,
+                                 int32_t* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+  __shared__ int32_t scan[256];
+  const int tid = threadIdx.x;
+  int run = 0;
+  for (int base = 0; base < E; base += 256) {
+    const int e = base + tid;
+    const int start = e < E ? offsets[e] : 0;
+    const int cnt = e < E ? offsets[e + 1] - start : 0;
+    const int nt = (cnt + bm - 1) / bm;
+    scan[tid] = nt;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {  // inclusive scan (Hillis-Steele)
+      const int v = tid >= d ? scan[tid - d] : 0;
+      __syncthreads();
+      scan[tid] += v;
+      __syncthreads();
+    }
+    const int first = run + scan[tid] - nt;
+    const int total = scan[255];
+    for (int i = 0; i < nt; ++i) {
+      int32_t* t = tiles + 4 * int64_t(first + i);
+      t[0] = e;
+      t[1] = start + i * bm;
+      t[2] = min(bm, cnt - i * bm);
+      t[3] = 0;
+    }
+    run += total;
+    __syncthreads();  // scan[] is rewritten by the next pass
+  }
+  if (tid == 0) n_tiles[0] = run;
+}
+
 // ---- activation quantiser: one workgroup per token.  PERM stores each group of 8 codes in
-// the order 0,2,4,6,1,3,5,7 and writes the block sums of the codes.
+// the order 0,2,4,6,1,3,5,7, writes the block sums of the codes, and has one more workgroup
+// (blockIdx.x == T) that builds the GEMV's tile list.
 template <bool PERM>
 __global__ void __launch_bounds__(256) quant_act_kernel(const uint16_t* __restrict__ x, int64_t K,
                                                         int8_t* __restrict__ q,
                                                         float* __restrict__ s_out,
-                                                        int32_t* __restrict__ xs) {
+                                                        int32_t* __restrict__ xs, int64_t T,
+                                                        const int32_t* __restrict__ offsets, int E,
+                                                        int bm, int32_t* __restrict__ tiles,
+                                                        int32_t* __restrict__ n_tiles) {
   __shared__ float red[4];
   const int tid = threadIdx.x;
   const int64_t t = blockIdx.x;
+  if (PERM && t == T) {  // uniform
+    int4_build_tiles(offsets, E, bm, tiles, n_tiles);
+    return;
+  }
   const uint16_t* xr = x + t * K;
   const int ngroups = int(K >> 3);
   float a = 0.f;
@@ -266,11 +310,9 @@ hipError_t launch_pack_int4(const uint16_t* w, int64_t n_elems, uint8_t* packed,
 }
 
 hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t K, int8_t* q, float* s,
-                            int32_t* xs, hipStream_t stream) {
-  if (xs)
-    hipLaunchKernelGGL(quant_act_kernel<true>, dim3(unsigned(T)), dim3(256), 0, stream, x, K, q, s, xs);
-  else
-    hipLaunchKernelGGL(quant_act_kernel<false>, dim3(unsigned(T)), dim3(256), 0, stream, x, K, q, s, xs);
+                            hipStream_t stream) {
+  hipLaunchKernelGGL(quant_act_kernel<false>, dim3(unsigned(T)), dim3(256), 0, stream, x, K, q, s,
+                     nullptr, T, nullptr, 0, 1, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -294,10 +336,11 @@ size_t int4_gemv_lds_bytes(int64_t T, int64_t K) {
 }
 
 hipError_t launch_int4_gemv(const Int4GemvLaunch& L, hipStream_t stream) {
-  hipError_t err = launch_quant_act(L.x, L.T, L.K, L.qx, L.sx, L.xs, stream);
-  if (err != hipSuccess) return err;
+  // one launch quantises the activations (T workgroups) and builds the tile list (one more)
   const int tr = int4_gemv_tile_rows(L.T);
-  err = launch_build_tiles(L.offsets, int(L.E), tr, L.tiles, L.n_tiles, stream);
+  hipLaunchKernelGGL(quant_act_kernel<true>, dim3(unsigned(L.T + 1)), dim3(256), 0, stream, L.x, L.K,
+                     L.qx, L.sx, L.xs, L.T, L.offsets, int(L.E), tr, L.tiles, L.n_tiles);
+  hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   I4Args a{};
   a.wq = L.wq;
