@@ -68,6 +68,7 @@ def _routed_problem(E, N, K, T, k, seed):
     (4, 160, 640, 40, 2),      # experts with more than 16 routed rows: several token tiles
     (8, 256, 1024, 64, 8),     # every expert busy
     (2, 128, 8192, 3, 1),      # the largest K
+    (4, 64, 8192, 20, 2),      # 16-row tiles at the largest K: 155 KB of LDS per workgroup
 ])
 def test_int4_gemv_matches_oracle(e4b, E, N, K, T, k):
     w, x, logits = _routed_problem(E, N, K, T, k, seed=E * 100 + T)
