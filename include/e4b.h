@@ -18,12 +18,16 @@
  * The forward multiplies directly on the packed bytes: codes are decoded in registers
  * and scaled per block, products accumulate in fp32, and only the final output is
  * rounded to bf16 (grouped-nf4-gemm 0.25.0 project description, opening section).  No
- * dequantised copy of a weight is ever written.
+ * dequantised copy of a weight is ever written.  Beside the forward: the input gradient of
+ * the grouped product on the same packed stacks (e4b_grouped_dgrad), and an int4-b32
+ * routed decode GEMV with exact integer block sums (e4b_pack_int4_b32, e4b_gemv_int4_b32).
  *
  * Conventions shared by every entry point
  *   - All tensor pointers are DEVICE pointers, owned by the caller, row-major and dense.
- *     The library allocates and frees nothing and keeps no state between calls; calls
- *     on different streams may run concurrently if their buffers do not overlap.
+ *     The library allocates and frees nothing; between calls it keeps only a per-device
+ *     cache of the architecture check and CU count (and, once a call needs it, the raised
+ *     dynamic-LDS limit of the int4 GEMV kernel).  Calls on different streams may run
+ *     concurrently if their buffers do not overlap.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue work
  *     and return; results are visible after the caller synchronises the stream.
  *   - Arguments are validated on the host before anything is enqueued.  A failed check
