@@ -118,9 +118,11 @@ int check_forward_shape(const e4b_moe_args* a) {
   if (a->T * a->k >= (int64_t(1) << 31)) return E4B_ERR_OVERFLOW;
   if (a->E >= (int64_t(1) << 31) || a->H >= (int64_t(1) << 31) || a->I >= (int64_t(1) << 30))
     return E4B_ERR_OVERFLOW;
-  // activation offsets inside the GEMMs are 32-bit element indices
+  // activation offsets inside the GEMMs are 32-bit element indices, weight offsets 32-bit
+  // byte offsets inside one expert's stack (I * H bytes for gate_up)
   if (a->T * a->H >= (int64_t(1) << 31) || a->T * a->k * a->I >= (int64_t(1) << 31))
     return E4B_ERR_OVERFLOW;
+  if (a->I * a->H >= (int64_t(1) << 31)) return E4B_ERR_OVERFLOW;
   return E4B_OK;
 }
 

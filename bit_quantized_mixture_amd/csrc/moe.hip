@@ -63,7 +63,13 @@ template <int FMT, bool GU, int BM, int WAVES>
 __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
   constexpr int ST = 4;  // pipeline depth
   constexpr int RB = BM / 32;
-  __shared__ __attribute__((aligned(16))) _Float16 lds[ST][BM][kBK];
+  // One LDS object holds the activation ring lds[ST][BM][kBK] and, after it, the weight rows
+  // of one 256-wide K group (128 packed bytes per row; wave w's 64 rows at w * 8 KB).
+  constexpr int kWRowBytes = 128;
+  constexpr int kRingBytes = ST * BM * kBK * 2;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kRingBytes + WAVES * 64 * kWRowBytes];
+  auto lds = reinterpret_cast<_Float16(*)[BM][kBK]>(smem);
+  uint8_t* const wl = smem + kRingBytes;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
@@ -91,8 +97,7 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
   }
   // ---- K order.  K is cut into groups of 256 (4 steps of 64).  Inside group G, step j,
   // lane half h supplies K elements [256G + 128h + 32j, +32): half h owns a contiguous
-  // 64-byte span of its weight row per group, so the group's four 16-byte loads of a lane
-  // hit the same cache lines back to back, and a group needs one pair of scale loads.  The
+  // 64-byte span of its weight row per group, so a group needs one pair of scale loads.  The
   // activation tile of step j is staged in the same order (chunk c of a row holds K
   // 256G + 128(c>>2) + 32j + 8(c&3)), so the MFMA k-slots of both operands agree.  The last
   // group may be partial: out-of-range pieces are loaded from a clamped address and get a
@@ -100,16 +105,44 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
   const int64_t kbytes = p.K >> 1;
   const int nk = int(p.K / kBK);          // real 64-wide steps (= NF4 blocks per row)
   const int ng = (nk + 3) >> 2;           // 256-wide groups
-  const uint8_t* wrow[2];
   const float* srow_nf4[2];
   const uint16_t* srow_mx[2];
 #pragma unroll
   for (int f = 0; f < 2; ++f) {
     const int64_t r = int64_t(e) * p.N + nrow[f];
-    wrow[f] = p.wq + r * kbytes;
     srow_nf4[f] = reinterpret_cast<const float*>(p.sc) + r * nk;
     srow_mx[f] = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(p.sc) + r * (2 * nk));
   }
+  // ---- weight staging: a group's rows come into LDS by direct buffer->LDS copies, 8 rows x
+  // 128 contiguous bytes per wave instruction (instead of 16-byte register loads that each
+  // touch 32 rows).  Copy i of wave w fills wave-local tile rows 8i .. 8i+7; lane l lands in
+  // row 8i + l/8, slot l%8, and brings the 16-byte piece (l%8) ^ ((row >> 1) & 7) of that
+  // row.  A fragment read (16 lanes, 16 consecutive rows, one piece) then meets 16 distinct
+  // (row parity, slot) pairs: with 128-byte rows on 64 four-byte banks, 16 distinct bank
+  // groups.  Tile row rr = 32f + c holds the weight row of lane c, fragment f.
+  const __amdgpu_buffer_rsrc_t wres =
+      buffer_rsrc(p.wq + int64_t(e) * p.N * kbytes, uint32_t(p.N * kbytes));
+  uint32_t wrow_off[8];   // row start (bytes from the expert's stack)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rr = 8 * i + (lane >> 3), f = rr >> 5, c = rr & 31;
+    int64_t row;
+    if (GU) {
+      const int64_t j = int64_t(nt) * (WAVES * 32) + wave * 32 + c;
+      const int64_t jc = j < p.I ? j : p.I - 1;
+      row = f == 0 ? (p.interleaved ? 2 * jc : jc) : (p.interleaved ? 2 * jc + 1 : p.I + jc);
+    } else {
+      const int64_t n = int64_t(nt) * (WAVES * 64) + wave * 64 + f * 32 + c;
+      row = n < p.N ? n : p.N - 1;
+    }
+    wrow_off[i] = uint32_t(row) * uint32_t(kbytes);
+  }
+  // (rr >> 1) & 7 = (4i + lane / 16) & 7: the piece depends on i only through its parity
+  uint32_t wpiece[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) wpiece[par] = 16u * uint32_t((lane & 7) ^ ((4 * par + (lane >> 4)) & 7));
+  const uint32_t wlast = uint32_t(kbytes - 16);
+  uint8_t* wl_wave = wl + wave * (64 * kWRowBytes);
 
   // ---- activation staging: global -> LDS directly (global_load_lds_dwordx4).  One
   // instruction of a wave fills 8 consecutive tile rows (64 lanes x 16 B); lane i writes
@@ -170,17 +203,35 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
       lds_dma16_buf(ares, 2 * (arow_off[j] + ko), &lds[buf][wave * ROWS_W + 8 * j][0]);
     }
   };
-  auto load_group = [&](int G, int slot) {
-    gld[slot] = G;
-    const int64_t o0 = int64_t(128) * G + 64 * half;
+  // The weight rows of group G into this wave's LDS tile (8 copies).  A piece past the end
+  // of its row (only in a partial last group) is fetched from the row's last 16 bytes
+  // instead; its scale is 0, so it contributes exactly 0.
+  auto dma_weights = [&](int G) {
+    const uint32_t go = 128u * uint32_t(G);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      typedef __attribute__((address_space(3))) void lds_void;
+      uint32_t o = go + wpiece[i & 1];
+      o = o < wlast ? o : wlast;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void*)(wl_wave + 1024 * i), 16,
+                                               int(wrow_off[i] + o), 0, 0, 0);
+    }
+  };
+  auto read_weights = [&](int slot) {
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
+      const int rr = 32 * f + col;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        int64_t o = o0 + 16 * j;
-        o = o < kbytes - 16 ? o : kbytes - 16;
-        bg[slot][f][j] = *reinterpret_cast<const u32x4*>(wrow[f] + o);
-      }
+      for (int j = 0; j < 4; ++j)
+        bg[slot][f][j] = *reinterpret_cast<const u32x4*>(
+            wl_wave + rr * kWRowBytes + 16 * ((4 * half + j) ^ ((rr >> 1) & 7)));
+    }
+  };
+  // Scales of group G into register slot `slot`.
+  auto load_group = [&](int G, int slot) {
+    gld[slot] = G;
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
       if (FMT == 0) {
         const int b0 = 4 * G + 2 * half;
         sraw[slot][f][0] = __float_as_uint(srow_nf4[f][b0 < nk ? b0 : nk - 1]);
@@ -206,7 +257,7 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
     const uint32_t byte = (sraw[slot][f][j >> 1] >> (8 * (j & 1))) & 0xFFu;
     return b < 2 * nk ? e8m0_to_f32(byte) : 0.0f;
   };
-  // Loads per wave: a group issues 2 x (4 weight + 2 scale) loads; a step NLD DMA.
+  // Loads per wave: a group issues 2 x 2 scale loads and 8 weight copies; a step NLD DMA.
   constexpr int kGroupOps = 12;
   auto afrag = [&](int buf, int rb, int s) {
     const int m = 32 * rb + col;
@@ -241,8 +292,13 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
     constexpr int J = decltype(j_c)::value;
     constexpr int NXT = (J + ST - 1) % ST;  // buffer freed by the previous step
     const int kb = 4 * G + J;
-    if (J == 0) load_group(G + 1 < ng ? G + 1 : ng - 1, 1);
     stage_a(kb + ST - 1, NXT);
+    if (J == 1) {  // the weight tile was read into registers in step 3 of the previous group
+      const int Gn = G + 1 < ng ? G + 1 : ng - 1;
+      load_group(Gn, 1);
+      dma_weights(Gn);
+    }
+    if (J == 3) read_weights(1);  // copied in step 1, landed before the barrier of step 2
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -270,9 +326,11 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
       bcur[1] = bnxt[1];
     }
     // Step kb+1's DMA (every wave's) has landed; this wave's reads of buffer J are done.
-    // Loads issued after DMA(kb+1): the DMA of steps kb-1 and kb, plus the group loads if
-    // one of those steps opened a group (group loads precede the step's DMA).
-    constexpr int kWait = 2 * NLD + (J < 2 ? kGroupOps : 0);
+    // Loads issued after DMA(kb+1): the DMA of steps kb-1 and kb, plus in step 1 the group
+    // ops issued after its DMA.  Step 2 waits further, for the group ops of step 1 (its
+    // weight copies are read at the top of step 3): only its own DMA may stay in flight.
+    // In step 3 the group ops are already done.
+    constexpr int kWait = J == 2 ? NLD : 2 * NLD + (J == 1 ? kGroupOps : 0);
     static_assert(kWait < 64, "vmcnt range");
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kWait));
@@ -293,10 +351,12 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
   };
 
   load_group(0, 0);
+  dma_weights(0);
 #pragma unroll
   for (int i = 0; i < ST - 1; ++i) stage_a(i, i);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * NLD));  // DMA of step 0 landed
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(2 * NLD));  // weights and DMA of step 0 landed
   __builtin_amdgcn_s_barrier();
+  read_weights(0);
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) afr[rb] = afrag(0, rb, 0);
   decode(bg[0], 0, 0, step_scale(0, 0, 0), step_scale(0, 1, 0), bcur);

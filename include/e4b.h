@@ -140,7 +140,8 @@ int e4b_route_permute(const float* logits, int64_t T, int64_t E, int32_t k, int3
                       int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
                       int32_t* sorted_slots, void* ws, size_t ws_bytes, void* stream);
 
-/* Arguments of e4b_moe_forward.  Sizes: H % 64 == 0, I % 64 == 0 (both formats). */
+/* Arguments of e4b_moe_forward.  Sizes: H % 64 == 0, I % 64 == 0 (both formats); T*H,
+ * T*k*I and I*H below 2^31 (E4B_ERR_OVERFLOW otherwise). */
 typedef struct e4b_moe_args {
   int32_t fmt;            /* e4b_fmt */
   int32_t k;              /* experts per token, as given to e4b_route_permute */

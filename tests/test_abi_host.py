@@ -120,6 +120,7 @@ def test_forward_rejects_bad_arguments(e4b):
     assert f(ws_bytes=1024) == ERR_WORKSPACE
     assert f(T=1 << 28, k=8) == ERR_OVERFLOW
     assert f(T=1 << 20, H=1 << 12) == ERR_OVERFLOW
+    assert f(T=1, H=1 << 16, I=1 << 15) == ERR_OVERFLOW   # one expert's stack >= 2^31 bytes
 
 
 def test_workspace_sizes_cover_the_intermediates(e4b):
