@@ -293,12 +293,12 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
     constexpr int NXT = (J + ST - 1) % ST;  // buffer freed by the previous step
     const int kb = 4 * G + J;
     stage_a(kb + ST - 1, NXT);
-    if (J == 1) {  // the weight tile was read into registers in step 3 of the previous group
+    if (J == 0) {  // the weight tile was read into registers in step 3 of the previous group
       const int Gn = G + 1 < ng ? G + 1 : ng - 1;
       load_group(Gn, 1);
       dma_weights(Gn);
     }
-    if (J == 3) read_weights(1);  // copied in step 1, landed before the barrier of step 2
+    if (J == 3) read_weights(1);  // copied in step 0, landed before the barrier of step 2
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -326,11 +326,10 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
       bcur[1] = bnxt[1];
     }
     // Step kb+1's DMA (every wave's) has landed; this wave's reads of buffer J are done.
-    // Loads issued after DMA(kb+1): the DMA of steps kb-1 and kb, plus in step 1 the group
-    // ops issued after its DMA.  Step 2 waits further, for the group ops of step 1 (its
-    // weight copies are read at the top of step 3): only its own DMA may stay in flight.
-    // In step 3 the group ops are already done.
-    constexpr int kWait = J == 2 ? NLD : 2 * NLD + (J == 1 ? kGroupOps : 0);
+    // Loads issued after DMA(kb+1): the DMA of steps kb-1 and kb, plus the group ops of
+    // step 0 (issued after its DMA) while step 0 is one of those two.  In step 2 this also
+    // covers the group's weight copies, read at the top of step 3.
+    constexpr int kWait = 2 * NLD + (J < 2 ? kGroupOps : 0);
     static_assert(kWait < 64, "vmcnt range");
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(kWait));
@@ -360,6 +359,8 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) afr[rb] = afrag(0, rb, 0);
   decode(bg[0], 0, 0, step_scale(0, 0, 0), step_scale(0, 1, 0), bcur);
+  // the weight tile's reads are complete before step 0 refills it
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
   for (int G = 0; G < ng; ++G) {
     kstep(G, std::integral_constant<int, 0>{});
     kstep(G, std::integral_constant<int, 1>{});
