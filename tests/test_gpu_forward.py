@@ -48,8 +48,9 @@ def test_small_layers(e4b, fmt, path, E, H, I, T, k):
 
 @pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
 @pytest.mark.parametrize("E,H,I,T,k", [
-    (4, 2880, 192, 5, 2),      # gate_up K = 2880: three K steps of the streaming kernel, last partial
-    (3, 128, 2112, 7, 1),      # down K = 2112: last step of 64
+    (4, 2880, 192, 5, 2),      # gate_up K = 2880: 12 K steps, the last partial; few items, so K is
+                               # split over the waves (some take two steps)
+    (3, 128, 2112, 7, 1),      # down K = 2112: last step of 64 (K split: wave 0 takes steps 0 and 8)
     (32, 512, 1024, 200, 4),   # more work items than resident workgroups: several items each
 ])
 def test_streaming_path_long_k_and_many_items(e4b, fmt, E, H, I, T, k):
