@@ -67,16 +67,12 @@ __device__ __forceinline__ float wave_sum(float x) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
 }
 
-// PL = logits per lane (E <= 64 * PL), a compile-time bound so the per-lane scans are short.
+// Top-k of one token's logits `row` by one wave; lane j < k gets the j-th pick and its
+// weight.  PL = logits per lane (E <= 64 * PL), a compile-time bound so the per-lane scans
+// are short.
 template <int PL>
-__global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int64_t T,
-                                                   int E, int k, int renorm,
-                                                   int32_t* __restrict__ ids,
-                                                   float* __restrict__ wts) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = int64_t(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6);
-  if (t >= T) return;  // whole wave exits together
-  const float* row = logits + t * E;
+__device__ __forceinline__ void topk_token(const float* __restrict__ row, int E, int k, int renorm,
+                                           int lane, int& id, float& wt) {
   float v[PL];
 #pragma unroll
   for (int i = 0; i < PL; ++i) {
@@ -118,9 +114,24 @@ __global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ log
     }
   }
   denom = wave_sum(denom);
+  id = my_id;
+  wt = ex / denom;
+}
+
+template <int PL>
+__global__ void __launch_bounds__(256) topk_kernel(const float* __restrict__ logits, int64_t T,
+                                                   int E, int k, int renorm,
+                                                   int32_t* __restrict__ ids,
+                                                   float* __restrict__ wts) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = int64_t(blockIdx.x) * (blockDim.x / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave exits together
+  int id;
+  float wt;
+  topk_token<PL>(logits + t * E, E, k, renorm, lane, id, wt);
   if (lane < k) {
-    ids[t * k + lane] = my_id;
-    wts[t * k + lane] = ex / denom;
+    ids[t * k + lane] = id;
+    wts[t * k + lane] = wt;
   }
 }
 
@@ -273,10 +284,82 @@ __global__ void __launch_bounds__(256) route_small_kernel(const int32_t* __restr
   scatter_range(ids, 0, T, k, e, base, slots, wave_tot);
 }
 
+// A few tokens (T <= kTinyT): route_small_kernel with the top-k folded in.  Every workgroup
+// (one per expert) computes the picks of all T tokens into LDS, one wave per token; workgroup
+// 0 also writes them out.  One launch for the whole router epilogue.
+constexpr int64_t kTinyT = 8;
+
+template <int PL>
+__global__ void __launch_bounds__(256) route_tiny_kernel(const float* __restrict__ logits,
+                                                         int64_t T, int E, int k, int renorm,
+                                                         int32_t* __restrict__ ids,
+                                                         float* __restrict__ wts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ slots) {
+  __shared__ int32_t sids[kTinyT * 64];
+  __shared__ int32_t red[2][4];
+  __shared__ int32_t wave_tot[4];
+  const int e = int(blockIdx.x);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int t = wave; t < int(T); t += 4) {
+    int id;
+    float wt;
+    topk_token<PL>(logits + int64_t(t) * E, E, k, renorm, lane, id, wt);
+    if (lane < k) {
+      sids[t * k + lane] = id;
+      if (e == 0) {
+        ids[t * k + lane] = id;
+        wts[t * k + lane] = wt;
+      }
+    }
+  }
+  __syncthreads();
+  const int n = int(T) * k;
+  int below = 0, mine = 0;
+  for (int i = tid; i < n; i += 256) {
+    const int v = sids[i];
+    below += v < e;
+    mine += v == e;
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    below += __shfl_xor(below, off);
+    mine += __shfl_xor(mine, off);
+  }
+  if (lane == 0) {
+    red[0][wave] = below;
+    red[1][wave] = mine;
+  }
+  __syncthreads();
+  const int base = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+  if (tid == 0) {
+    offsets[e] = base;
+    if (e == E - 1) offsets[E] = base + red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  }
+  scatter_range(sids, 0, T, k, e, base, slots, wave_tot);
+}
+
 hipError_t launch_route(const float* logits, int64_t T, int64_t E, int k, bool renorm,
                         int32_t* ids, float* w, int32_t* offsets, int32_t* slots, int32_t* cc,
                         hipStream_t stream) {
   const int chunks = route_chunks(T);
+  if (T > 0 && T <= kTinyT) {
+    const unsigned g = unsigned(E);
+    const int rn = renorm ? 1 : 0;
+    if (E <= 64)
+      hipLaunchKernelGGL(route_tiny_kernel<1>, dim3(g), dim3(256), 0, stream, logits, T, int(E), k, rn,
+                         ids, w, offsets, slots);
+    else if (E <= 128)
+      hipLaunchKernelGGL(route_tiny_kernel<2>, dim3(g), dim3(256), 0, stream, logits, T, int(E), k, rn,
+                         ids, w, offsets, slots);
+    else if (E <= 256)
+      hipLaunchKernelGGL(route_tiny_kernel<4>, dim3(g), dim3(256), 0, stream, logits, T, int(E), k, rn,
+                         ids, w, offsets, slots);
+    else
+      hipLaunchKernelGGL(route_tiny_kernel<kMaxExpertsPerLane>, dim3(g), dim3(256), 0, stream, logits,
+                         T, int(E), k, rn, ids, w, offsets, slots);
+    return hipGetLastError();
+  }
   if (T > 0) {
     const int64_t blocks = (T + 3) / 4;
     const unsigned g = unsigned(blocks);

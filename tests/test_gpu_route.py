@@ -40,6 +40,8 @@ def test_route_skewed_has_empty_experts(e4b):
 
 
 @pytest.mark.parametrize("T,E,k", [(1, 1, 1), (5, 1, 1), (1, 8, 8), (33, 8, 8), (1, 128, 8),
+                                   # up to 8 tokens: top-k folded into the one-launch router
+                                   (8, 1024, 64), (8, 200, 5), (2, 65, 3), (6, 300, 64), (9, 128, 8),
                                    (300, 1024, 64), (70, 65, 3), (257, 16, 2),
                                    # several 1024-token chunks of the counting sort, ragged last
                                    (2500, 1024, 8), (3073, 3, 2), (1024, 7, 7), (1025, 1, 1)])
@@ -56,11 +58,13 @@ def test_route_ties_and_signed_zero(e4b):
     lg[2] = 1.0
     _check(e4b, lg, 4)
     _check(e4b, lg, 12)
+    _check(e4b, lg[:6], 4)     # few tokens: the one-launch router
 
 
 def test_route_without_renormalisation(e4b):
     rng = np.random.default_rng(3)
     _check(e4b, rng.standard_normal((64, 32), dtype=np.float32) * 3, 4, renormalize=False)
+    _check(e4b, rng.standard_normal((3, 32), dtype=np.float32) * 3, 4, renormalize=False)
 
 
 def test_route_empty_batch(e4b):
