@@ -20,9 +20,10 @@
 // (GU: 32 gate + 32 matching up rows per wave, so SwiGLU is formed in registers).  Each
 // wave owns all BM rows x 64 weight rows and keeps its accumulators in registers
 // (v_mfma_f32_32x32x16_f16).  The activation tile (BM x 64 fp16 per K step) comes through a
-// 4-stage LDS ring filled by direct buffer->LDS loads and is shared by the waves; each lane
-// streams its own weight rows' packed bytes straight from HBM (64 contiguous bytes per
-// 256-wide K group) and decodes them in registers.
+// 4-stage LDS ring filled by direct buffer->LDS loads and is shared by the waves.  The
+// packed weight rows of each wave come through a wave-private LDS tile, one 256-wide K group
+// at a time (also by direct buffer->LDS copies); each lane reads its 64-byte span of its rows
+// from there into registers and decodes it in registers.
 #include <type_traits>
 
 #include "e4b_device.h"
@@ -180,10 +181,10 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
   }
 
   // ---- software pipeline.  Step kb (= 4G + j) reads LDS buffer j; the activation DMA of
-  // step kb + ST - 1 is issued at the top of step kb.  Weights and scales of group G + 1
-  // are loaded at the top of group G into the "next" registers.  The step count is padded
-  // to whole groups.
-  const int nk_pad = 4 * ng;
+  // step kb + ST - 1 is issued at the top of step kb.  At the top of group G the scales of
+  // group G + 1 are loaded into the "next" registers and its weight rows copied into the
+  // weight tile, which step 3 of group G reads into the "next" registers.  The step count
+  // is padded to whole groups.
   u32x4 bg[2][2][4];   // [cur/next][fragment][step in group]
   // Raw scale words of a half's span (loaded values are only combined where they are used,
   // so no wait is forced at load time).  NF4: absmax of blocks b0, b0+1 (float bits);
@@ -367,7 +368,6 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
     kstep(G, std::integral_constant<int, 2>{});
     kstep(G, std::integral_constant<int, 3>{});
   }
-  (void)nk_pad;
   // drain the DMA issued past the last step before the workgroup's LDS is released
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
 
