@@ -5,7 +5,8 @@
 //
 // * Persistent workgroups of 8 waves, two per CU (16 waves per CU, four per SIMD, so one
 //   wave's compute overlaps the others' loads).  A work item is (tile of <= 16 routed rows of
-//   one expert, block of 128 * RB weight rows); each wave owns RB row blocks of 16 rows.  A
+//   one expert, block of 128 * RB weight rows); each wave owns RB row blocks of 16 rows (the
+//   launches use RB = 1, which measured faster than 2).  A
 //   workgroup walks its items and, inside each item, K in steps of 256, as one flat sequence.
 // * 16x16x32 f16 MFMA with the weights as the A operand and the routed activations as B (16
 //   columns): D[row, token] += sum_k W[row, k] * X[token, k].  One activation fragment read
@@ -52,7 +53,6 @@ constexpr int kLutBytes = kNf4LutBytes;            // 64 KB: 256 pairs x 64 lane
 constexpr int kWgPerCu = 2;                         // LDS: 80 KB per workgroup with the table
 constexpr int kStages = 2;                          // register sets in the load ring
 constexpr int kActLoads = kTok / (2 * kWaves);      // activation loads (two rows each) per wave
-constexpr int kMaxRB = kWaves >= 8 ? 2 : 4;         // row blocks per wave (VGPR budget)
 
 static_assert(kTok == 16, "one MFMA pass of 16 routed rows per tile");
 static_assert(kActLoads >= 1 && kTok == 2 * kWaves * kActLoads, "activation rows per wave");
@@ -576,8 +576,10 @@ hipError_t launch_rb(const GemvArgs& g, const TileList& tl, const MoeLaunch& L, 
   return hipGetLastError();
 }
 
-// Row blocks per wave: the largest of kMaxRB, ..., 2, 1 that still gives every resident
-// workgroup an item (the tile count is a device value; its host-side upper bound is used).
+// One row block per wave.  Two (one activation fragment feeding two row blocks) were measured
+// slower on every decode layer tried, by 2-20 % for gate_up: 128 experts of 1536 x 2048 at 16
+// and 64 tokens, 8 experts of 28672 x 4096 at 4 to 32 tokens.  The item count uses the
+// host-side upper bound of the tile count (a device value).
 template <int FMT, bool GU, bool SLOT>
 hipError_t launch_stage(const GemvArgs& g, const TileList& tl, const MoeLaunch& L, void* out,
                         int64_t n_out, hipStream_t stream) {
@@ -589,10 +591,6 @@ hipError_t launch_stage(const GemvArgs& g, const TileList& tl, const MoeLaunch& 
     const int64_t per_item = kWaves * rb * per_block;
     return tl.max_tiles * ((n_out + per_item - 1) / per_item);
   };
-  if constexpr (kMaxRB >= 4) {
-    if (items(4) >= wgs) return launch_rb<FMT, GU, 4, SLOT>(g, tl, L, out, n_out, wgs, stream);
-  }
-  if (items(2) >= wgs) return launch_rb<FMT, GU, 2, SLOT>(g, tl, L, out, n_out, wgs, stream);
   if (SLOT || 3 * items(1) >= wgs)
     return launch_rb<FMT, GU, 1, SLOT>(g, tl, L, out, n_out, wgs, stream);
   // fewer items than a third of the resident workgroups (measured on a 128-expert layer,
