@@ -30,7 +30,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libe4b.so")
 if not os.path.exists(lib_path):
     raise ImportError(
-        f"{lib_path} is not built; build it with `python -m bit_quantized_mixture_amd.build` "
+        f"{lib_path} is not built; build it with `python bit_quantized_mixture_amd/build.py` "
         "(hipcc, gfx950).  There is no non-HIP implementation.")
 _lib = ctypes.CDLL(lib_path)
 

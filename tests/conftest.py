@@ -18,7 +18,11 @@ def e4b():
     """The binding, with libe4b.so built in-tree first if it is missing."""
     lib = os.path.join(ROOT, "bit_quantized_mixture_amd", "libe4b.so")
     if not os.path.exists(lib):
-        from bit_quantized_mixture_amd.build import build
-        build()
+        import importlib.util
+        spec = importlib.util.spec_from_file_location(
+            "_e4b_build", os.path.join(ROOT, "bit_quantized_mixture_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
     import bit_quantized_mixture_amd as m
     return m
