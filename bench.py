@@ -7,16 +7,19 @@ grouped gate_up GEMM + SwiGLU, grouped down GEMM, weighted combine) on weights t
 already packed and resident in HBM.  Inputs are the seeded synthetic tensors of
 moe_inputs.py.  Prints ONE JSON line on stdout; progress goes to stderr.
 
-The headline workload is the Mixtral-shaped NF4 prefill layer (E=8, H=4096, I=14336, top-2,
-T=4096).  The same line carries, under "secondary", the skewed 64-expert prefill layer, the
-MXFP4 layer (also run as the MXFP4 family's expert variant: interleaved gate/up rows, clamped
-GLU, per-expert biases) and the 128-expert decode layer at T = 64, 16, 4, 1 (warm, and cold with the
-256 MB Infinity Cache flushed by reading 1 GiB before every step; eager launches with per-stage HIP events,
-and the same step replayed from a HIP graph), and a float64 CPU-oracle baseline timed on a
-bounded sample of the headline workload.  Also under "secondary": the grouped dgrad on the
-headline layer's packed down and gate_up stacks with its own routing, and the int4-b32 routed
-decode GEMV (exact integer accumulation) on the decode layer's gate_up stack at T = 64 and 1
-and on one dense [14336, 4096] matrix at M = 1, in GB/s of weight streaming.
+The headline workload is the largest prefill layer, the skewed 64-expert NF4 layer (E=64,
+H=4096, I=1536, top-8, T=16384, Zipf-biased routing with 20 empty experts).  The same line
+carries, under "secondary", the Mixtral-shaped NF4 prefill layer (E=8, H=4096, I=14336, top-2,
+T=4096), the MXFP4 layer (also run as the MXFP4 family's expert variant: interleaved gate/up
+rows, clamped GLU, per-expert biases) and the 128-expert decode layer at T = 64, 16, 4, 1 (warm,
+and cold with the 256 MB Infinity Cache flushed by reading 1 GiB before every step; eager
+launches with per-stage HIP events, and the same step replayed from a HIP graph), and a float64
+CPU-oracle baseline timed on a bounded sample of the headline workload.  Also under
+"secondary": the grouped dgrad on the Mixtral-shaped layer's packed down and gate_up stacks
+with its own routing, and the int4-b32 routed decode GEMV (exact integer accumulation) on the
+decode layer's gate_up stack at T = 64 and 1 and on one dense [14336, 4096] matrix at M = 1, in
+GB/s of weight streaming.  "hbm_ceiling" holds the rate of a plain device copy and of a plain
+streaming read measured in the same run, beside the published 8 TB/s.
 """
 from __future__ import annotations
 
@@ -412,6 +415,30 @@ def int4_report(torch, e4b, wl, T: int, steps: int, warmup: int) -> dict:
             "algorithmic_bytes": nbytes, "achieved_gbs": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS}
 
 
+def hbm_ceiling(torch, nbytes: int = 2 << 30, reps: int = 10) -> dict:
+    """Measured ceilings beside the published HBM peak: a plain device-to-device copy of
+    `nbytes` (read + written bytes per second) and a plain streaming read (a sum over the same
+    buffer), each the mean of `reps` launches timed with HIP events on the current stream."""
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    b = torch.empty_like(a)
+    res = {}
+    for key, fn, moved in (("copy_gbs", lambda: b.copy_(a), 2 * nbytes), ("read_gbs", lambda: a.sum(), nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        res[key] = moved / (t0.elapsed_time(t1) / reps / 1e3) / 1e9
+    res["bytes"] = nbytes
+    res["published_gbs"] = PEAK_HBM_GBS
+    del a, b
+    torch.cuda.empty_cache()
+    return res
+
+
 def fmt_rep(key, rep):
     rl = rep["roofline"]
     s = (f"[bench] {key}: {rep['ms_per_step']:.4f} ms/step, {rep['tokens_per_s']:.0f} tok/s, "
@@ -426,7 +453,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixtral_nf4_prefill", choices=list(WORKLOADS))
+    ap.add_argument("--workload", default="skewed_nf4_prefill", choices=list(WORKLOADS))
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--secondary", default="all",
                     help="comma list of secondary sections to run: dgrad, prefill (the skewed and "
@@ -455,18 +482,24 @@ def main():
     secondary = {}
     sections = set() if args.no_secondary else (
         {"dgrad", "prefill", "int4", "decode"} if args.secondary == "all" else set(args.secondary.split(",")))
-    if "dgrad" in sections:
-        secondary[wl.name + "_dgrad"] = dg = dgrad_report(torch, layer, max(args.steps, 10), args.warmup)
-        log(f"[bench] {wl.name} dgrad: " + ", ".join(
-            f"{k} {v['ms']:.3f} ms {v['tflops']:.1f} TFLOP/s ({100 * v['frac_of_mfma_peak']:.1f}%)" for k, v in dg.items()))
     del layer
     torch.cuda.empty_cache()
+    ceiling = hbm_ceiling(torch)
+    log(f"[bench] HBM ceiling: copy {ceiling['copy_gbs']:.0f} GB/s, read {ceiling['read_gbs']:.0f} GB/s")
 
-    if "prefill" in sections:
-        for name in ("skewed_nf4_prefill", "mxfp4_moe"):
-            if name == wl.name:
-                continue
-            lay = Layer(e4b, torch, WORKLOADS[name])
+    dgrad_on = "mixtral_nf4_prefill"
+    for name in ("mixtral_nf4_prefill", "skewed_nf4_prefill", "mxfp4_moe"):
+        run_fwd = "prefill" in sections and name != wl.name
+        run_dgrad = "dgrad" in sections and name == dgrad_on
+        if not (run_fwd or run_dgrad):
+            continue
+        lay = Layer(e4b, torch, WORKLOADS[name])
+        if run_dgrad:
+            secondary[name + "_dgrad"] = dg = dgrad_report(torch, lay, max(args.steps, 10), args.warmup)
+            log(f"[bench] {name} dgrad: " + ", ".join(
+                f"{k} {v['ms']:.3f} ms {v['tflops']:.1f} TFLOP/s ({100 * v['frac_of_mfma_peak']:.1f}%)"
+                for k, v in dg.items()))
+        if run_fwd:
             secondary[name] = batch_report(torch, lay, WORKLOADS[name].T, max(args.steps, 10), args.warmup)
             log(fmt_rep(name, secondary[name]))
             if name == "mxfp4_moe":
@@ -480,8 +513,8 @@ def main():
                 secondary[key] = batch_report(torch, lay, wv.T, max(args.steps, 10), args.warmup,
                                               variant=variant)
                 log(fmt_rep(key, secondary[key]))
-            del lay
-            torch.cuda.empty_cache()
+        del lay
+        torch.cuda.empty_cache()
     if "int4" in sections:
         for name, T in (("finegrained_int4_decode", 64), ("finegrained_int4_decode", 1),
                         ("dense_int4_decode", 1)):
@@ -526,6 +559,7 @@ def main():
         "stage_ms": main_rep["stage_ms"],
         "roofline": dict(main_rep["roofline"]),
         "cpu_baseline": cpu,
+        "hbm_ceiling": ceiling,
         "gpu_pack_gbs": pack_gbs,
         "secondary": secondary,
         "kernel_source_sha": kernel_source_sha(),

@@ -119,9 +119,46 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def _need(t, name, dtypes, shape=None):
+class _on_stream:
+    """Context for the binding's own allocations (outputs and workspaces it creates): they are
+    made on the stream the kernels run on, so the caching allocator does not hand the memory to
+    other work before those kernels are done.  A raw stream handle (not a torch stream) other
+    than the current stream cannot be tracked: the caller then passes every buffer."""
+
+    def __init__(self, stream):
+        self.stream = stream
+        self.ctx = None
+
+    def __enter__(self):
+        s = self.stream
+        if s is None:
+            return self
+        if isinstance(s, torch.cuda.Stream):
+            self.ctx = torch.cuda.stream(s)
+            self.ctx.__enter__()
+        elif int(s) != torch.cuda.current_stream().cuda_stream:
+            self.ctx = False
+        return self
+
+    def alloc(self, *a, **kw):
+        if self.ctx is False:
+            raise ValueError("pass a torch.cuda.Stream, or preallocate every output and workspace, "
+                             "when the work runs on a raw stream handle other than the current stream")
+        return torch.empty(*a, **kw)
+
+    def __exit__(self, *exc):
+        if self.ctx:
+            self.ctx.__exit__(*exc)
+        return False
+
+
+def _need(t, name, dtypes, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor, not {type(t).__name__}")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if t.dtype not in dtypes:
@@ -136,13 +173,16 @@ _BF16 = (torch.bfloat16, torch.uint16, torch.int16)
 def e4b_pack_nf4(w, packed=None, absmax=None, stream=None):
     """w [E, N, K] bf16 -> (packed uint8 [E, N, K/2], absmax float32 [E, N, K/64])."""
     _need(w, "w", _BF16)
+    if w.dim() != 3:
+        raise ValueError(f"w must be [E, N, K], got shape {tuple(w.shape)}")
     E, N, K = w.shape
-    if packed is None:
-        packed = torch.empty((E, N, K // 2), dtype=torch.uint8, device=w.device)
-    if absmax is None:
-        absmax = torch.empty((E, N, K // 64), dtype=torch.float32, device=w.device)
-    _need(packed, "packed", (torch.uint8,), (E, N, K // 2))
-    _need(absmax, "absmax", (torch.float32,), (E, N, K // 64))
+    with _on_stream(stream) as st:
+        if packed is None:
+            packed = st.alloc((E, N, K // 2), dtype=torch.uint8, device=w.device)
+        if absmax is None:
+            absmax = st.alloc((E, N, K // 64), dtype=torch.float32, device=w.device)
+    _need(packed, "packed", (torch.uint8,), (E, N, K // 2), w.device)
+    _need(absmax, "absmax", (torch.float32,), (E, N, K // 64), w.device)
     _check("e4b_pack_nf4", _c_pack_nf4(_ptr(w), E, N, K, _ptr(packed), _ptr(absmax), _stream(stream)))
     return packed, absmax
 
@@ -150,13 +190,16 @@ def e4b_pack_nf4(w, packed=None, absmax=None, stream=None):
 def e4b_pack_mxfp4(w, blocks=None, scales=None, stream=None):
     """w [E, N, K] bf16 -> (blocks uint8 [E, N, K/32, 16], scales uint8 [E, N, K/32])."""
     _need(w, "w", _BF16)
+    if w.dim() != 3:
+        raise ValueError(f"w must be [E, N, K], got shape {tuple(w.shape)}")
     E, N, K = w.shape
-    if blocks is None:
-        blocks = torch.empty((E, N, K // 32, 16), dtype=torch.uint8, device=w.device)
-    if scales is None:
-        scales = torch.empty((E, N, K // 32), dtype=torch.uint8, device=w.device)
-    _need(blocks, "blocks", (torch.uint8,), (E, N, K // 32, 16))
-    _need(scales, "scales", (torch.uint8,), (E, N, K // 32))
+    with _on_stream(stream) as st:
+        if blocks is None:
+            blocks = st.alloc((E, N, K // 32, 16), dtype=torch.uint8, device=w.device)
+        if scales is None:
+            scales = st.alloc((E, N, K // 32), dtype=torch.uint8, device=w.device)
+    _need(blocks, "blocks", (torch.uint8,), (E, N, K // 32, 16), w.device)
+    _need(scales, "scales", (torch.uint8,), (E, N, K // 32), w.device)
     _check("e4b_pack_mxfp4", _c_pack_mxfp4(_ptr(w), E, N, K, _ptr(blocks), _ptr(scales), _stream(stream)))
     return blocks, scales
 
@@ -171,22 +214,25 @@ def e4b_route_permute(logits, k: int, renormalize: bool = True, ws=None, stream=
     """logits [T, E] float32 -> (topk_ids [T,k] i32, topk_w [T,k] f32, expert_offsets [E+1] i32,
     sorted_slots [T*k] i32).  `out`: optional preallocated (ids, w, offsets, slots)."""
     _need(logits, "logits", (torch.float32,))
+    if logits.dim() != 2:
+        raise ValueError(f"logits must be [T, E], got shape {tuple(logits.shape)}")
     T, E = logits.shape
     dev = logits.device
-    if out is None:
-        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-        w = torch.empty((T, k), dtype=torch.float32, device=dev)
-        offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
-        slots = torch.empty((T * k,), dtype=torch.int32, device=dev)
-    else:
-        ids, w, offsets, slots = out
-        _need(ids, "topk_ids", (torch.int32,), (T, k))
-        _need(w, "topk_w", (torch.float32,), (T, k))
-        _need(offsets, "expert_offsets", (torch.int32,), (E + 1,))
-        _need(slots, "sorted_slots", (torch.int32,), (T * k,))
-    if ws is None:
-        need = e4b_route_workspace_bytes(T, E, k)
-        ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    with _on_stream(stream) as st:
+        if out is None:
+            out = (st.alloc((T, k), dtype=torch.int32, device=dev),
+                   st.alloc((T, k), dtype=torch.float32, device=dev),
+                   st.alloc((E + 1,), dtype=torch.int32, device=dev),
+                   st.alloc((T * k,), dtype=torch.int32, device=dev))
+        if ws is None:
+            need = e4b_route_workspace_bytes(T, E, k)
+            ws = st.alloc((max(need, 256),), dtype=torch.uint8, device=dev)
+    ids, w, offsets, slots = out
+    _need(ids, "topk_ids", (torch.int32,), (T, k), dev)
+    _need(w, "topk_w", (torch.float32,), (T, k), dev)
+    _need(offsets, "expert_offsets", (torch.int32,), (E + 1,), dev)
+    _need(slots, "sorted_slots", (torch.int32,), (T * k,), dev)
+    _need(ws, "ws", (torch.uint8,), device=dev)
     flags = E4B_ROUTE_RENORMALIZE if renormalize else 0
     _check("e4b_route_permute", _c_route(
         _ptr(logits), T, E, k, flags, _ptr(ids), _ptr(w), _ptr(offsets), _ptr(slots),
@@ -217,6 +263,13 @@ def e4b_moe_workspace_bytes(fmt, E: int, H: int, I: int, T: int, k: int, path: i
     return n.value
 
 
+def _stack_shapes(fmt: int, E: int, N: int, K: int):
+    """(codes shape, codes dtype, scales shape, scales dtype) of a packed [E, N, K] stack."""
+    if fmt == E4B_FMT_NF4:
+        return (E, N, K // 2), torch.uint8, (E, N, K // 64), torch.float32
+    return (E, N, K // 32, 16), torch.uint8, (E, N, K // 32), torch.uint8
+
+
 def e4b_moe_forward(fmt, x, w_gu, s_gu, w_dn, s_dn, topk_w, expert_offsets, sorted_slots, k: int,
                     out=None, out_f32=None, ws=None, path: int = E4B_PATH_AUTO, stream=None,
                     stage_events=None, act: str = "swiglu", interleaved: bool = False,
@@ -228,25 +281,52 @@ def e4b_moe_forward(fmt, x, w_gu, s_gu, w_dn, s_dn, topk_w, expert_offsets, sort
     `b_dn` [E, H] float32 biases (or None): the expert variant flags of include/e4b.h.
     `stage_events`: None, or 6 torch.cuda.Event (enable_timing=True), each recorded once
     beforehand so that it exists; the call records them around its 5 stages.
+    Every tensor is checked (device, dtype, contiguity, the shape implied by fmt, E, H, I, T, k)
+    before the library is called.
     """
+    if fmt not in _FMT:
+        raise ValueError(f"fmt must be 'nf4' or 'mxfp4', not {fmt!r}")
+    f = _FMT[fmt]
     _need(x, "x", _BF16)
-    T, H = x.shape
-    E = expert_offsets.numel() - 1
-    I = w_dn.shape[2] * (2 if w_dn.dim() == 3 else 32)
     dev = x.device
-    if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    if out_f32 is True:
-        out_f32 = torch.empty((T, H), dtype=torch.float32, device=dev)
-    if ws is None:
-        need = e4b_moe_workspace_bytes(fmt, E, H, I, T, k, path)
-        ws = torch.empty((max(need, 256),), dtype=torch.uint8, device=dev)
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, H], got shape {tuple(x.shape)}")
+    T, H = x.shape
+    _need(expert_offsets, "expert_offsets", (torch.int32,), device=dev)
+    if expert_offsets.dim() != 1 or expert_offsets.numel() < 2:
+        raise ValueError("expert_offsets must be [E + 1] with E >= 1")
+    E = expert_offsets.numel() - 1
+    _need(w_dn, "w_dn", (torch.uint8,), device=dev)
+    if f == E4B_FMT_NF4 and w_dn.dim() == 3:
+        I = w_dn.shape[2] * 2
+    elif f == E4B_FMT_MXFP4 and w_dn.dim() == 4 and w_dn.shape[3] == 16:
+        I = w_dn.shape[2] * 32
+    else:
+        raise ValueError(f"w_dn of shape {tuple(w_dn.shape)} is not a {fmt} down stack")
+    for name, t, (N, K) in (("gate_up", (w_gu, s_gu), (2 * I, H)), ("down", (w_dn, s_dn), (H, I))):
+        cs, cd, ss, sd = _stack_shapes(f, E, N, K)
+        _need(t[0], f"w_{name}", (cd,), cs, dev)
+        _need(t[1], f"s_{name}", (sd,), ss, dev)
+    _need(topk_w, "topk_w", (torch.float32,), (T, k), dev)
+    _need(sorted_slots, "sorted_slots", (torch.int32,), (T * k,), dev)
     if act not in ("swiglu", "clamped_glu"):
         raise ValueError(f"act must be 'swiglu' or 'clamped_glu', not {act!r}")
-    flags = path | (E4B_ACT_CLAMPED_GLU if act == "clamped_glu" else 0) | (E4B_GU_INTERLEAVED if interleaved else 0)
     for name, b, n in (("b_gu", b_gu, (E, 2 * I)), ("b_dn", b_dn, (E, H))):
         if b is not None:
-            _need(b, name, (torch.float32,), n)
+            _need(b, name, (torch.float32,), n, dev)
+    with _on_stream(stream) as st:
+        if out is None:
+            out = st.alloc((T, H), dtype=torch.bfloat16, device=dev)
+        if out_f32 is True:
+            out_f32 = st.alloc((T, H), dtype=torch.float32, device=dev)
+        if ws is None:
+            need = e4b_moe_workspace_bytes(fmt, E, H, I, T, k, path)
+            ws = st.alloc((max(need, 256),), dtype=torch.uint8, device=dev)
+    _need(out, "out", _BF16, (T, H), dev)
+    if out_f32 is not None:
+        _need(out_f32, "out_f32", (torch.float32,), (T, H), dev)
+    _need(ws, "ws", (torch.uint8,), device=dev)
+    flags = path | (E4B_ACT_CLAMPED_GLU if act == "clamped_glu" else 0) | (E4B_GU_INTERLEAVED if interleaved else 0)
     a = _moe_args(fmt, x, w_gu, s_gu, w_dn, s_dn, topk_w, expert_offsets, sorted_slots, E, H, I, k,
                   out, out_f32, ws, flags)
     a.b_gu = None if b_gu is None else b_gu.data_ptr()
@@ -281,21 +361,33 @@ def e4b_grouped_dgrad(fmt, g, w, s, expert_offsets, out_f32=None, out=False, ws=
     out=True to get the bf16 copy.
     """
     _need(g, "g", _BF16)
+    if g.dim() != 2:
+        raise ValueError(f"g must be [S, N], got shape {tuple(g.shape)}")
     S, N = g.shape
+    if w.dim() not in (3, 4):
+        raise ValueError(f"w of shape {tuple(w.shape)} is not a packed stack")
     E = w.shape[0]
     K = w.shape[2] * (2 if w.dim() == 3 else 32)
     if w.shape[1] != N:
         raise ValueError(f"w has {w.shape[1]} rows per expert, g has {N} columns")
-    _need(expert_offsets, "expert_offsets", (torch.int32,), (E + 1,))
     dev = g.device
-    if out_f32 is None:
-        out_f32 = torch.empty((S, K), dtype=torch.float32, device=dev)
-    if out is True:
-        out = torch.empty((S, K), dtype=torch.bfloat16, device=dev)
-    elif out is False:
-        out = None
-    if ws is None:
-        ws = torch.empty((max(e4b_dgrad_workspace_bytes(fmt, E, N, K, S), 256),), dtype=torch.uint8, device=dev)
+    _need(expert_offsets, "expert_offsets", (torch.int32,), (E + 1,), dev)
+    cs, cd, ss, sd = _stack_shapes(_FMT[fmt], E, N, K)
+    _need(w, "w", (cd,), cs, dev)
+    _need(s, "s", (sd,), ss, dev)
+    with _on_stream(stream) as st:
+        if out_f32 is None:
+            out_f32 = st.alloc((S, K), dtype=torch.float32, device=dev)
+        if out is True:
+            out = st.alloc((S, K), dtype=torch.bfloat16, device=dev)
+        elif out is False:
+            out = None
+        if ws is None:
+            ws = st.alloc((max(e4b_dgrad_workspace_bytes(fmt, E, N, K, S), 256),), dtype=torch.uint8, device=dev)
+    _need(out_f32, "out_f32", (torch.float32,), (S, K), dev)
+    if out is not None:
+        _need(out, "out", _BF16, (S, K), dev)
+    _need(ws, "ws", (torch.uint8,), device=dev)
     a = _dgrad_args(fmt, E, N, K, S)
     a.g, a.w, a.s, a.expert_offsets = g.data_ptr(), w.data_ptr(), s.data_ptr(), expert_offsets.data_ptr()
     a.out_f32 = out_f32.data_ptr()
@@ -308,11 +400,16 @@ def e4b_grouped_dgrad(fmt, g, w, s, expert_offsets, out_f32=None, out=False, ws=
 def e4b_pack_int4_b32(w, packed=None, scales=None, stream=None):
     """w [E, N, K] bf16 -> (packed uint8 [E, N, K/2], scales float16 [E, N, K/32])."""
     _need(w, "w", _BF16)
+    if w.dim() != 3:
+        raise ValueError(f"w must be [E, N, K], got shape {tuple(w.shape)}")
     E, N, K = w.shape
-    if packed is None:
-        packed = torch.empty((E, N, K // 2), dtype=torch.uint8, device=w.device)
-    if scales is None:
-        scales = torch.empty((E, N, K // 32), dtype=torch.float16, device=w.device)
+    with _on_stream(stream) as st:
+        if packed is None:
+            packed = st.alloc((E, N, K // 2), dtype=torch.uint8, device=w.device)
+        if scales is None:
+            scales = st.alloc((E, N, K // 32), dtype=torch.float16, device=w.device)
+    _need(packed, "packed", (torch.uint8,), (E, N, K // 2), w.device)
+    _need(scales, "scales", (torch.float16, torch.int16), (E, N, K // 32), w.device)
     _check("e4b_pack_int4_b32", _c_pack_int4(_ptr(w), E, N, K, _ptr(packed), _ptr(scales), _stream(stream)))
     return packed, scales
 
@@ -320,9 +417,12 @@ def e4b_pack_int4_b32(w, packed=None, scales=None, stream=None):
 def e4b_quantize_act_int8(x, stream=None):
     """x [T, K] bf16 -> (q int8 [T, K], s float32 [T]): per-token int8 activations."""
     _need(x, "x", _BF16)
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, K], got shape {tuple(x.shape)}")
     T, K = x.shape
-    q = torch.empty((T, K), dtype=torch.int8, device=x.device)
-    sc = torch.empty((max(T, 1),), dtype=torch.float32, device=x.device)[:T]
+    with _on_stream(stream) as st:
+        q = st.alloc((T, K), dtype=torch.int8, device=x.device)
+        sc = st.alloc((max(T, 1),), dtype=torch.float32, device=x.device)[:T]
     _check("e4b_quantize_act_int8", _c_quant_act(_ptr(x), T, K, _ptr(q), _ptr(sc), _stream(stream)))
     return q, sc
 
@@ -356,11 +456,14 @@ def e4b_gemv_int4_b32(w, s, x, k: int, expert_offsets, sorted_slots, out=None, w
     _need(s, "s", (torch.float16, torch.int16), (E, N, K // 32))
     _need(expert_offsets, "expert_offsets", (torch.int32,), (E + 1,))
     _need(sorted_slots, "sorted_slots", (torch.int32,), (T * k,))
-    if out is None:
-        out = torch.empty((T * k, N), dtype=torch.float32, device=x.device)
-    if ws is None:
-        ws = torch.empty((max(e4b_int4_gemv_workspace_bytes(E, N, K, T, k), 256),),
-                         dtype=torch.uint8, device=x.device)
+    with _on_stream(stream) as st:
+        if out is None:
+            out = st.alloc((T * k, N), dtype=torch.float32, device=x.device)
+        if ws is None:
+            ws = st.alloc((max(e4b_int4_gemv_workspace_bytes(E, N, K, T, k), 256),),
+                          dtype=torch.uint8, device=x.device)
+    _need(out, "out", (torch.float32,), (T * k, N), x.device)
+    _need(ws, "ws", (torch.uint8,), device=x.device)
     a = _int4_args(E, N, K, T, k)
     a.x, a.w, a.s = x.data_ptr(), w.data_ptr(), s.data_ptr()
     a.expert_offsets, a.sorted_slots = expert_offsets.data_ptr(), sorted_slots.data_ptr()

@@ -152,8 +152,8 @@ __global__ void __launch_bounds__(kThreads) dgrad_kernel(DgradArgs p) {
     for (int r = 0; r < 2; ++r) {
       if (FMT == 0) {
         nf4_decode8(R.w[r], d[r]);
-        const float scf = __uint_as_float(R.s[r]);
-        const f16x2 s16 = f16x2{(_Float16)scf, (_Float16)scf};
+        const _Float16 sh = (_Float16)(__uint_as_float(R.s[r]) * kNf4ScaleUp);
+        const f16x2 s16 = f16x2{sh, sh};
 #pragma unroll
         for (int i = 0; i < 4; ++i) d[r][i] = pk_mul_f16(d[r][i], s16);
       } else {
@@ -249,7 +249,7 @@ __global__ void __launch_bounds__(kThreads) dgrad_kernel(DgradArgs p) {
         const int row = 128 * rh + 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3);
         if (row < rows) {
           const int64_t o = int64_t(row0 + row) * p.K + k;
-          const float v = acc[rb][f][r];
+          const float v = FMT == 0 ? acc[rb][f][r] * kNf4ScaleDown : acc[rb][f][r];
           p.out_f32[o] = v;
           if (p.out) p.out[o] = f32_to_bf16_rne(v);
         }

@@ -123,6 +123,14 @@ __device__ __forceinline__ void nf4_decode8(uint32_t w, uint32_t out[4]) {
   out[3] = perm(hi_odd, lo_odd, 0x07030602u);    // elements 5, 7
 }
 
+// NF4 block scales enter the fp16 decode multiplied by 2^8, and every fp32 product sum over
+// such weights is multiplied by 2^-8 before it is used (both exact powers of two).  The decoded
+// operand fp16(C) * fp16(absmax * 2^8) then stays an fp16 normal number for every nonzero code
+// (smallest |C| = 0.0796) while 2^-18 <= absmax <= 255: the window of real weight scales, down to
+// weights 2^-12 below N(0, 0.02), instead of [2^-10, 65504] without the shift.
+constexpr float kNf4ScaleUp = 256.0f;
+constexpr float kNf4ScaleDown = 1.0f / 256.0f;
+
 // Multiply two packed fp16 by the same fp16 scale (v_pk_mul_f16).
 __device__ __forceinline__ uint32_t pk_mul_f16(uint32_t v, f16x2 s) {
   f16x2 r = __builtin_bit_cast(f16x2, v) * s;

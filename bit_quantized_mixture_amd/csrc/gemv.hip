@@ -243,8 +243,8 @@ __device__ __forceinline__ void compute_step(int64_t krem, int lane, const StepR
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
     if (FMT == 0) {
-      const float sc = valid ? __uint_as_float(R.sv[b]) : 0.0f;
-      s16[b] = f16x2{(_Float16)sc, (_Float16)sc};
+      const _Float16 sh = (_Float16)(valid ? __uint_as_float(R.sv[b]) * kNf4ScaleUp : 0.0f);
+      s16[b] = f16x2{sh, sh};
     } else {
       smx[b][0] = valid ? e8m0_to_f32(R.sv[b] & 0xFFu) : 0.0f;
       smx[b][1] = valid ? e8m0_to_f32((R.sv[b] >> 8) & 0xFFu) : 0.0f;
@@ -299,11 +299,12 @@ __device__ __forceinline__ void compute_step(int64_t krem, int lane, const StepR
 
 // Results of 16-row block `blk` of the expert's output rows (gate_up: 8 gate rows and the 8
 // matching up rows).  acc: element i = D[row 4g + i of the block, token r].
-template <bool GU, bool SLOT>
+template <int FMT, bool GU, bool SLOT>
 __device__ __forceinline__ void store_block(const GemvArgs& p, const Ptrs& pt,
                                             const StepInfo& st, int32_t blk, int lane,
-                                            const f32x4& acc) {
+                                            f32x4 acc) {
   const int r = lane & 15, g = lane >> 4;
+  if (FMT == 0) acc *= kNf4ScaleDown;  // NF4 sums carry the 2^8 of the scale shift
   if (GU) {
     // rows 0-7 are gate rows, 8-15 the matching up rows: lane groups 0/1 hold gate values,
     // 2/3 the up values of the same (j, token)
@@ -412,10 +413,10 @@ __global__ void __launch_bounds__(kThreads)
         if (ci[rs].last) {
           const int32_t blk0 = ci[rs].rb * (kWaves * RB) + wave * RB;
           if (RB == 1) {
-            store_block<GU, SLOT>(p, pt, ci[rs], blk0, lane, acc[0] + acc[1]);
+            store_block<FMT, GU, SLOT>(p, pt, ci[rs], blk0, lane, acc[0] + acc[1]);
           } else {
 #pragma unroll
-            for (int b = 0; b < RB; ++b) store_block<GU, SLOT>(p, pt, ci[rs], blk0 + b, lane, acc[b]);
+            for (int b = 0; b < RB; ++b) store_block<FMT, GU, SLOT>(p, pt, ci[rs], blk0 + b, lane, acc[b]);
           }
 #pragma unroll
           for (int a = 0; a < NA; ++a) acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -504,8 +505,8 @@ __global__ void __launch_bounds__(kThreads)
     f16x2 s16{};
     float smx[2] = {0.f, 0.f};
     if (FMT == 0) {
-      const float sc = valid ? __uint_as_float(sv) : 0.0f;
-      s16 = f16x2{(_Float16)sc, (_Float16)sc};
+      const _Float16 sh = (_Float16)(valid ? __uint_as_float(sv) * kNf4ScaleUp : 0.0f);
+      s16 = f16x2{sh, sh};
     } else {
       smx[0] = valid ? e8m0_to_f32(sv & 0xFFu) : 0.0f;
       smx[1] = valid ? e8m0_to_f32((sv >> 8) & 0xFFu) : 0.0f;
@@ -535,7 +536,7 @@ __global__ void __launch_bounds__(kThreads)
   if (wi == 0 && blk < n_blocks) {
     f32x4 sum = part[64 * wave + lane];
     for (int w = 1; w < W; ++w) sum += part[64 * (wave + w) + lane];
-    store_block<GU, false>(p, Ptrs{tiles, tok, out}, st, blk, lane, sum);
+    store_block<FMT, GU, false>(p, Ptrs{tiles, tok, out}, st, blk, lane, sum);
   }
 }
 

@@ -273,7 +273,8 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
       uint32_t d[4];
       if (FMT == 0) {
         nf4_decode8(bsl[f][j][s], d);
-        const f16x2 s16 = f16x2{(_Float16)scs[f], (_Float16)scs[f]};
+        const _Float16 sh = (_Float16)(scs[f] * kNf4ScaleUp);
+        const f16x2 s16 = f16x2{sh, sh};
 #pragma unroll
         for (int i = 0; i < 4; ++i) d[i] = pk_mul_f16(d[i], s16);
       } else {
@@ -373,7 +374,15 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
 
   // ---- epilogue.  Accumulator element r of a 32x32 block: row 8*(r/4) + 4*half + r%4,
   // column = col.  The plain SwiGLU / unbiased forms are kept as their own branches: the
-  // stores then take their data straight from the accumulators.
+  // stores then take their data straight from the accumulators.  NF4 sums carry the 2^8 of
+  // the scale shift (kNf4ScaleUp), taken out here.
+  if (FMT == 0) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      acc[rb][0] *= kNf4ScaleDown;
+      acc[rb][1] *= kNf4ScaleDown;
+    }
+  }
   if (GU) {
     if (!nvalid[0]) return;
     const int64_t j = int64_t(nt) * (WAVES * 32) + wave * 32 + col;

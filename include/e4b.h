@@ -36,6 +36,24 @@
  *   - Every pointer must be 16-byte aligned.  bf16 values are passed as uint16_t bits.
  *   - Faults inside kernels surface at the caller's next synchronisation; launch
  *     failures return E4B_ERR_HIP.
+ *
+ * Operand ranges of the forward and the dgrad.  The matrix products take fp16 operands with
+ * fp32 accumulation (bf16 inputs are converted exactly where they fit).  The stated output
+ * tolerance holds while every operand is an fp16 normal number:
+ *   x, g    bf16 activations / gradients: |v| <= 65504.  Larger values become +-inf in fp16
+ *           and the output shows inf or NaN; |v| < 2^-14 is carried as an fp16 subnormal
+ *           (absolute error <= 2^-25).
+ *   NF4     decoded weight = fp16(C[code]) * fp16(absmax * 2^8), product sums scaled by 2^-8
+ *           (both exact): every nonzero decoded weight is an fp16 normal (relative error
+ *           <= 2^-11 per rounding, two roundings) for 2^-18 <= absmax <= 255.  Larger absmax
+ *           overflows; smaller absmax decodes to fp16 subnormals (absolute error <= 2^-33 per
+ *           weight).
+ *   MXFP4   decoded weight = e2m1 * 2^e, exact in fp16 for scale exponents e = byte - 127 in
+ *           [-23, 13]; above 13 large codes overflow, below -23 small codes are rounded.
+ *   h       the activation between the two products is stored as fp16: |h| <= 65504 (larger
+ *           becomes inf); below 2^-14 it is an fp16 subnormal (absolute error <= 2^-25).
+ * These ranges are not checked on the device: a check would need a device-to-host read,
+ * which the asynchronous calls never make.
  */
 #ifndef E4B_H_
 #define E4B_H_
@@ -68,7 +86,7 @@ typedef enum e4b_fmt { E4B_FMT_NF4 = 0, E4B_FMT_MXFP4 = 1 } e4b_fmt;
  * (128-row tiles below a mean of 256 rows, 256-row tiles from there).  The choice depends only on host-known sizes; no device value is read back. */
 #define E4B_PATH_AUTO 0x0
 #define E4B_PATH_GEMM 0x1 /* MFMA grouped GEMM, 128- or 256-row tiles (an expert's last <= 1/4
-                           * tile of rows goes to 32-row tiles) */
+                           * tile of rows goes to 16-row tiles of the streaming kernel) */
 #define E4B_PATH_GEMV 0x2 /* small-M streaming path: 16-row tiles, each expert's weights streamed
                            * once per 16 routed rows */
 #define E4B_PATH_MASK 0x3
@@ -146,7 +164,7 @@ typedef struct e4b_moe_args {
   int32_t fmt;            /* e4b_fmt */
   int32_t k;              /* experts per token, as given to e4b_route_permute */
   int64_t E, H, I, T;
-  const uint16_t* x;      /* [T, H] bf16 bits; values must lie in fp16 range */
+  const uint16_t* x;      /* [T, H] bf16 bits; |x| <= 65504 (see "Operand ranges") */
   const uint8_t* w_gu;    /* NF4 [E, 2I, H/2]  | MXFP4 [E, 2I, H/32, 16]; rows 0..I-1 gate, I..2I-1 up */
   const void* s_gu;       /* NF4 float [E, 2I, H/64] | MXFP4 uint8 [E, 2I, H/32] */
   const uint8_t* w_dn;    /* NF4 [E, H, I/2]   | MXFP4 [E, H, I/32, 16] */

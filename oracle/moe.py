@@ -85,12 +85,14 @@ def expert_mlp(x: np.ndarray, w_gu: np.ndarray, w_dn: np.ndarray, act: str = "sw
 
 def forward(fmt: str, x_bits: np.ndarray, gu_packed, gu_scales, dn_packed, dn_scales,
             ids: np.ndarray, weights: np.ndarray, tokens=None, act: str = "swiglu",
-            interleaved: bool = False, b_gu=None, b_dn=None) -> np.ndarray:
+            interleaved: bool = False, b_gu=None, b_dn=None, experts=None) -> np.ndarray:
     """out [len(tokens), H] float64 for the selected tokens (all tokens by default).
 
     Experts are visited one at a time; each expert's slice of the packed stacks is
     decoded and applied to the tokens (among the selected ones) routed to it.  act,
     interleaved, b_gu [E, 2I] and b_dn [E, H] select the expert variant (expert_mlp).
+    `experts` (optional) restricts the sum to the slots routed to those experts, so the
+    output over a partition of the experts is the sum of the partial outputs.
     """
     T, k = ids.shape
     tokens = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
@@ -100,6 +102,8 @@ def forward(fmt: str, x_bits: np.ndarray, gu_packed, gu_scales, dn_packed, dn_sc
     sub_ids = np.asarray(ids)[tokens]
     sub_w = np.asarray(weights, np.float64)[tokens]
     for e in np.unique(sub_ids):
+        if experts is not None and int(e) not in experts:
+            continue
         rows, js = np.nonzero(sub_ids == e)
         w_gu = decode_expert(fmt, gu_packed, gu_scales, int(e))
         w_dn = decode_expert(fmt, dn_packed, dn_scales, int(e))
@@ -143,4 +147,51 @@ def dgrad(fmt: str, packed: np.ndarray, scales: np.ndarray, g_bits: np.ndarray,
         lo, hi = int(offsets[e]), int(offsets[e + 1])
         if hi > lo:
             out[lo:hi] = g[lo:hi] @ decode_expert(fmt, packed, scales, e)
+    return out
+
+
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """float32 values rounded to bfloat16 (round to nearest even), returned as float32."""
+    bits = f64_to_bf16_bits(np.asarray(a, np.float32).astype(np.float64))
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def forward_dequant_bf16(fmt: str, x_bits: np.ndarray, gu_packed, gu_scales, dn_packed, dn_scales,
+                         ids: np.ndarray, weights: np.ndarray, tokens=None, act: str = "swiglu",
+                         interleaved: bool = False, b_gu=None, b_dn=None, experts=None) -> np.ndarray:
+    """The unfused comparator of the fidelity claim (grouped-nf4-gemm 0.25.0 project
+    description, "What is measured", first row: the fused path is more accurate than
+    dequantise-to-bf16).  Each expert's weights are decoded and rounded to bf16, then used in
+    bf16 matrix products with float32 accumulation whose results a bf16 framework returns in
+    bf16: G and U (bias added before the rounding), h = act(G, U) computed from them and
+    rounded to bf16, and Y (bias likewise).  The top-k weighted sum is float64.
+    Arguments as `forward`; returns float64 [len(tokens), H].
+    """
+    T, k = ids.shape
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens, np.int64)
+    x = bf16_bits_to_f64(np.asarray(x_bits)[tokens]).astype(np.float32)
+    H = x.shape[1]
+    out = np.zeros((len(tokens), H), np.float64)
+    sub_ids = np.asarray(ids)[tokens]
+    sub_w = np.asarray(weights, np.float64)[tokens]
+    for e in np.unique(sub_ids):
+        if experts is not None and int(e) not in experts:
+            continue
+        rows, js = np.nonzero(sub_ids == e)
+        w_gu = round_bf16(decode_expert(fmt, gu_packed, gu_scales, int(e)).astype(np.float32))
+        w_dn = round_bf16(decode_expert(fmt, dn_packed, dn_scales, int(e)).astype(np.float32))
+        I = w_dn.shape[1]
+        gu = x[rows] @ w_gu.T
+        if b_gu is not None:
+            gu = gu + np.asarray(b_gu, np.float32)[int(e)]
+        gu = round_bf16(gu)
+        g, u = (gu[:, 0::2], gu[:, 1::2]) if interleaved else (gu[:, :I], gu[:, I:])
+        g64, u64 = g.astype(np.float64), u.astype(np.float64)
+        h = silu(g64) * u64 if act == "swiglu" else clamped_glu(g64, u64)
+        h = round_bf16(h.astype(np.float32))
+        y = h @ w_dn.T
+        if b_dn is not None:
+            y = y + np.asarray(b_dn, np.float32)[int(e)]
+        y = round_bf16(y)
+        out[rows] += sub_w[rows, js][:, None] * y.astype(np.float64)
     return out

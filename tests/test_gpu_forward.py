@@ -182,3 +182,33 @@ def test_swiglu_with_one_bias_and_interleaved_rows(e4b, flags):
     for kw in (dict(b_gu=b_gu), dict(b_dn=b_dn), dict(interleaved=True, b_gu=b_gu)):
         out, out32 = layer.forward(flags, **kw)
         assert_rows_within_tolerance(out32, layer.oracle_out(**kw), f"flags={flags:#x} {sorted(kw)}")
+
+
+def test_binding_rejects_mismatched_tensors(e4b, tiny):
+    """Every tensor of e4b_moe_forward is checked against the shape fmt, E, H, I, T and k
+    imply before the library is called (no launch on inconsistent buffers)."""
+    ids, w, off, slots = tiny.route()
+    torch.cuda.synchronize()
+    args = dict(fmt="nf4", x=tiny.x, w_gu=tiny.gp, s_gu=tiny.gs, w_dn=tiny.dp, s_dn=tiny.ds,
+                topk_w=w, expert_offsets=off, sorted_slots=slots, k=tiny.k)
+
+    def bad(**kw):
+        a = dict(args, **kw)
+        with pytest.raises((ValueError, TypeError)):
+            e4b.e4b_moe_forward(a.pop("fmt"), a.pop("x"), a.pop("w_gu"), a.pop("s_gu"), a.pop("w_dn"),
+                                a.pop("s_dn"), a.pop("topk_w"), a.pop("expert_offsets"),
+                                a.pop("sorted_slots"), a.pop("k"), **a)
+
+    bad(fmt="mxfp4")                                   # NF4 stacks read as MXFP4
+    bad(expert_offsets=off[:-1].contiguous())          # one expert too few
+    bad(w_gu=tiny.gp[:, : tiny.gp.shape[1] // 2].contiguous())   # half the gate_up rows
+    bad(s_dn=tiny.ds.to(torch.float16))                # wrong scale dtype
+    bad(topk_w=w[:, :1].contiguous())                  # k = 1 weights for k = 2
+    bad(sorted_slots=slots[:-1].contiguous())
+    bad(x=tiny.x.t())                                  # not contiguous
+    bad(out=torch.empty((tiny.T, tiny.H + 64), dtype=torch.bfloat16, device="cuda:0"))
+    bad(out_f32=torch.empty((tiny.T, tiny.H), dtype=torch.float16, device="cuda:0"))
+    bad(w_dn=tiny.dp.cpu())                            # host tensor
+    out, _ = e4b.e4b_moe_forward(**{**args, "fmt": "nf4"})
+    torch.cuda.synchronize()
+    assert out.shape == (tiny.T, tiny.H)

@@ -184,7 +184,51 @@ def test_nf4_power_of_two_invariance(j):
     assert np.array_equal(a2, (a * np.float32(2.0 ** j)).astype(np.float32))
 
 
+def test_nf4_nibble_order_hand_written_bytes():
+    """The bitsandbytes gemm_4bit layout named by the grouped-nf4-gemm 0.25.0 project description
+    (opening section): bitsandbytes' blockwise 4-bit quantiser shifts the code of element 2p
+    into the high nibble of byte p and puts element 2p+1 in the low nibble.  The bytes below are
+    written by hand from that rule, not computed."""
+    C = nf4.NF4_CODEBOOK
+    row = np.zeros(64, np.float32)
+    row[0], row[1] = 1.0, -1.0        # codes 15 and 0 (absmax 1)
+    row[2], row[3] = 0.0, C[8]        # codes 7 and 8
+    row[4], row[5] = C[3], C[12]      # codes 3 and 12
+    packed, absmax = nf4.quantize_pack(row[None, :])
+    assert absmax[0, 0] == 1.0
+    want = bytes([0xF0, 0x78, 0x3C] + [0x77] * 29)
+    assert packed[0].tobytes() == want
+    # and the decoder reads them back the same way: byte 0xC3 is element 2p = C[12], 2p+1 = C[3]
+    raw = np.full((1, 32), 0x77, np.uint8)
+    raw[0, 0] = 0xC3
+    back = nf4.dequantize(raw, np.array([[2.0]], np.float32))
+    assert back[0, 0] == np.float32(C[12] * 2.0) and back[0, 1] == np.float32(C[3] * 2.0)
+    assert np.all(back[0, 2:] == 0.0)
+
+
 # ----------------------------------------------------------------------------- MXFP4
+
+def test_mxfp4_nibble_order_hand_written_bytes():
+    """The released-checkpoint byte order named by the grouped-nf4-gemm 0.25.0 project description
+    (opening section, MXFP4 on a checkpoint's exact released bytes): byte p of a 32-block holds
+    element 2p in its low nibble and element 2p+1 in its high nibble (the order in which the
+    gpt-oss checkpoints' e2m1 blocks are unpacked, low nibble first).  An e2m1 code is
+    sign | exponent(2) | mantissa(1).  The bytes below are written by hand from those rules."""
+    row = np.zeros(32, np.float32)
+    row[0], row[1] = 6.0, -0.5        # codes 0b0111 = 7 and 0b1001 = 9; amax 6 -> exponent 0
+    row[2], row[3] = 1.5, -4.0        # codes 0b0011 = 3 and 0b1110 = 14
+    row[4], row[5] = 0.0, 2.0         # codes 0 and 0b0100 = 4
+    blocks, scales = mxfp4.quantize_pack(row[None, :])
+    assert scales[0, 0] == 127
+    want = bytes([0x97, 0xE3, 0x40] + [0x00] * 13)
+    assert blocks[0, 0].tobytes() == want
+    # decode direction: byte 0x5A is element 0 = code 0xA (-1.0), element 1 = code 5 (3.0)
+    raw = np.zeros((1, 1, 16), np.uint8)
+    raw[0, 0, 0] = 0x5A
+    back = mxfp4.dequantize(raw, np.array([[128]], np.uint8))   # scale 2^1
+    assert back[0, 0] == -2.0 and back[0, 1] == 6.0 and np.all(back[0, 2:] == 0.0)
+
+
 
 def test_e2m1_bit_fields_give_ocp_values():
     mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
@@ -546,3 +590,44 @@ def test_dgrad_matches_pure_python_loops_and_empty_experts():
                 ref = sum(gf[p][n] * W[n][k] for n in range(16))
                 assert abs(out[p][k] - ref) <= 1e-12 * max(1.0, abs(ref))
     assert offsets[2] == offsets[1]  # expert 1 has no rows, and nothing is written for it
+
+
+# ----------------------------------------------------------------------------- forward helpers
+
+def test_forward_over_a_partition_of_the_experts_sums_to_the_full_output():
+    fmt = "nf4"
+    x, gp, gs, dp, ds, ids, w = _tiny_problem(fmt, E=4, T=9, k=2, seed=3)
+    full = moe.forward(fmt, x, gp, gs, dp, ds, ids, w)
+    parts = moe.forward(fmt, x, gp, gs, dp, ds, ids, w, experts={0, 2}) + \
+        moe.forward(fmt, x, gp, gs, dp, ds, ids, w, experts={1, 3})
+    assert np.max(np.abs(parts - full)) <= 1e-12 * np.max(np.abs(full))
+    assert np.all(moe.forward(fmt, x, gp, gs, dp, ds, ids, w, experts=set()) == 0.0)
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
+def test_dequant_bf16_comparator_matches_torch_bf16_layers(fmt):
+    """The fidelity comparator against the same computation written with torch's CPU bf16
+    matrix products (float32 accumulation, bf16 results) and bf16 tensors: equal up to the
+    one-ulp differences that a different float32 summation order can flip."""
+    x, gp, gs, dp, ds, ids, w = _tiny_problem(fmt, E=3, H=64, I=128, T=7, k=2, seed=4)
+    got = moe.forward_dequant_bf16(fmt, x, gp, gs, dp, ds, ids, w)
+    xt = torch.from_numpy(moe.bf16_bits_to_f64(x)).to(torch.bfloat16)
+    ref = torch.zeros(got.shape, dtype=torch.float64)
+    for e in range(3):
+        t, j = np.nonzero(ids == e)
+        if len(t) == 0:
+            continue
+        wg = torch.from_numpy(moe.decode_expert(fmt, gp, gs, e)).to(torch.bfloat16)
+        wd = torch.from_numpy(moe.decode_expert(fmt, dp, ds, e)).to(torch.bfloat16)
+        gu = xt[torch.from_numpy(t)] @ wg.T
+        I = wd.shape[1]
+        g, u = gu[:, :I].double(), gu[:, I:].double()
+        h = (g / (1 + torch.exp(-g)) * u).float().to(torch.bfloat16)
+        y = (h @ wd.T).double()
+        ref[torch.from_numpy(t)] += torch.from_numpy(w[t, j])[:, None] * y
+    ref = ref.numpy()
+    rms = np.sqrt(np.mean(ref ** 2))
+    assert np.max(np.abs(got - ref)) <= 2.0 ** -6 * rms
+    # and it is a bf16 computation: visibly less exact than the float64 definition
+    exact = moe.forward(fmt, x, gp, gs, dp, ds, ids, w)
+    assert np.sqrt(np.mean((got - exact) ** 2)) > 1e-4 * rms
