@@ -237,7 +237,8 @@ def kernel_source_sha() -> str:
 def load_counters(workload: str) -> dict:
     """HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (profiles/hbm_traffic.txt,
     already scaled by the copy-kernel calibration), used only while the kernel sources are
-    the ones the counters were taken on."""
+    the ones the counters were taken on.  `workload` is the workload name, with _T<T> appended
+    for a batch size other than the workload's own."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
     out = {}
     if not os.path.exists(path):
@@ -313,8 +314,8 @@ def batch_report(torch, layer: Layer, T: int, steps: int, warmup: int, flush: in
     n_active = b.active_experts()
     m = measure(torch, b, steps, warmup, flush)
     # the counters were taken at each workload's own T; other batch sizes get none
-    same_T = wl.T == WORKLOADS[wl.name].T
-    rl = roofline(wl, n_active, m, load_counters(wl.name) if same_T and not flush else None)
+    key = wl.name if wl.T == WORKLOADS[wl.name].T else f"{wl.name}_T{wl.T}"
+    rl = roofline(wl, n_active, m, None if flush else load_counters(key))
     S = wl.T * wl.k
     ms = m["ms_per_step"]
     rep = {
@@ -454,6 +455,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="skewed_nf4_prefill", choices=list(WORKLOADS))
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="batch size of the headline workload (default: the workload's own T)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--secondary", default="all",
                     help="comma list of secondary sections to run: dgrad, prefill (the skewed and "
@@ -474,7 +477,9 @@ def main():
         sys.exit(1)
 
     wl = WORKLOADS[args.workload]
-    log(f"[bench] device {torch.cuda.get_device_name(0)}; workload {wl.name}")
+    if args.tokens:
+        wl = wl.with_T(args.tokens)
+    log(f"[bench] device {torch.cuda.get_device_name(0)}; workload {wl.name}, T = {wl.T}")
     layer = Layer(e4b, torch, wl)
     pack_gbs = layer.pack_bytes / layer.pack_s / 1e9
     main_rep = batch_report(torch, layer, wl.T, args.steps, args.warmup, flags=args.flags)
