@@ -16,7 +16,7 @@ __all__ = [
     "E4BError", "E4B_FMT_NF4", "E4B_FMT_MXFP4", "E4B_PATH_AUTO", "E4B_PATH_GEMM", "E4B_PATH_GEMV",
     "E4B_ROUTE_RENORMALIZE", "E4B_ACT_CLAMPED_GLU", "E4B_GU_INTERLEAVED", "lib_path", "e4b_version", "e4b_status_string", "e4b_pack_nf4",
     "e4b_pack_mxfp4", "e4b_route_workspace_bytes", "e4b_route_permute", "e4b_moe_workspace_bytes",
-    "e4b_moe_forward", "MoeArgs", "e4b_dgrad_workspace_bytes", "e4b_grouped_dgrad", "DgradArgs",
+    "e4b_moe_forward", "e4b_moe_forward_noalloc", "e4b_noalloc_scratch_bytes", "MoeArgs", "e4b_dgrad_workspace_bytes", "e4b_grouped_dgrad", "DgradArgs",
 ]
 
 E4B_FMT_NF4, E4B_FMT_MXFP4 = 0, 1
@@ -82,6 +82,8 @@ _c_route_ws = _decl("e4b_route_workspace_bytes", [_i64, _i64, _i32, ctypes.POINT
 _c_route = _decl("e4b_route_permute", [_vp, _i64, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
 _c_moe_ws = _decl("e4b_moe_workspace_bytes", [ctypes.POINTER(MoeArgs), ctypes.POINTER(_sz)])
 _c_moe_forward = _decl("e4b_moe_forward", [ctypes.POINTER(MoeArgs), _vp])
+_c_moe_forward_noalloc = _decl("e4b_moe_forward_noalloc", [ctypes.POINTER(MoeArgs), _vp])
+_c_noalloc_bytes = _decl("e4b_noalloc_scratch_bytes", [], _sz)
 _c_dgrad_ws = _decl("e4b_dgrad_workspace_bytes", [ctypes.POINTER(DgradArgs), ctypes.POINTER(_sz)])
 _c_dgrad = _decl("e4b_grouped_dgrad", [ctypes.POINTER(DgradArgs), _vp])
 _c_pack_int4 = _decl("e4b_pack_int4_b32", [_vp, _i64, _i64, _i64, _vp, _vp, _vp])
@@ -284,6 +286,15 @@ def e4b_moe_forward(fmt, x, w_gu, s_gu, w_dn, s_dn, topk_w, expert_offsets, sort
     Every tensor is checked (device, dtype, contiguity, the shape implied by fmt, E, H, I, T, k)
     before the library is called.
     """
+    return _moe_forward_call(_c_moe_forward, "e4b_moe_forward", fmt, x, w_gu, s_gu, w_dn, s_dn,
+                             topk_w, expert_offsets, sorted_slots, k, out, out_f32, ws, path, stream,
+                             stage_events, act, interleaved, b_gu, b_dn)
+
+
+def _moe_forward_call(cfn, cname, fmt, x, w_gu, s_gu, w_dn, s_dn, topk_w, expert_offsets,
+                      sorted_slots, k, out, out_f32, ws, path, stream, stage_events, act,
+                      interleaved, b_gu, b_dn):
+    noalloc = cfn is _c_moe_forward_noalloc
     if fmt not in _FMT:
         raise ValueError(f"fmt must be 'nf4' or 'mxfp4', not {fmt!r}")
     f = _FMT[fmt]
@@ -319,13 +330,14 @@ def e4b_moe_forward(fmt, x, w_gu, s_gu, w_dn, s_dn, topk_w, expert_offsets, sort
             out = st.alloc((T, H), dtype=torch.bfloat16, device=dev)
         if out_f32 is True:
             out_f32 = st.alloc((T, H), dtype=torch.float32, device=dev)
-        if ws is None:
+        if ws is None and not noalloc:
             need = e4b_moe_workspace_bytes(fmt, E, H, I, T, k, path)
             ws = st.alloc((max(need, 256),), dtype=torch.uint8, device=dev)
     _need(out, "out", _BF16, (T, H), dev)
     if out_f32 is not None:
         _need(out_f32, "out_f32", (torch.float32,), (T, H), dev)
-    _need(ws, "ws", (torch.uint8,), device=dev)
+    if not noalloc:
+        _need(ws, "ws", (torch.uint8,), device=dev)
     flags = path | (E4B_ACT_CLAMPED_GLU if act == "clamped_glu" else 0) | (E4B_GU_INTERLEAVED if interleaved else 0)
     a = _moe_args(fmt, x, w_gu, s_gu, w_dn, s_dn, topk_w, expert_offsets, sorted_slots, E, H, I, k,
                   out, out_f32, ws, flags)
@@ -336,7 +348,7 @@ def e4b_moe_forward(fmt, x, w_gu, s_gu, w_dn, s_dn, topk_w, expert_offsets, sort
             raise ValueError("stage_events needs 6 events")
         handles = (_vp * 6)(*[ev.cuda_event for ev in stage_events])
         a.stage_events = ctypes.cast(handles, ctypes.POINTER(_vp))
-    _check("e4b_moe_forward", _c_moe_forward(ctypes.byref(a), _stream(stream)))
+    _check(cname, cfn(ctypes.byref(a), _stream(stream)))
     return out, out_f32
 
 
@@ -471,3 +483,24 @@ def e4b_gemv_int4_b32(w, s, x, k: int, expert_offsets, sorted_slots, out=None, w
     a.ws, a.ws_bytes = ws.data_ptr(), ws.numel() * ws.element_size()
     _check("e4b_gemv_int4_b32", _c_int4_gemv(ctypes.byref(a), _stream(stream)))
     return out
+
+
+def e4b_noalloc_scratch_bytes() -> int:
+    return _c_noalloc_bytes()
+
+
+def e4b_moe_forward_noalloc(fmt, x, w_gu, s_gu, w_dn, s_dn, topk_w, expert_offsets, sorted_slots,
+                            k: int, out, out_f32=None, path: int = E4B_PATH_AUTO, stream=None,
+                            act: str = "swiglu", interleaved: bool = False, b_gu=None, b_dn=None):
+    """e4b_moe_forward without a workspace argument and without any allocation: the library's
+    fixed device scratch is the workspace.  `out` (bf16 [T, H]) must be given; `out_f32`
+    (float32 [T, H]) may be.  Raises E4BError (E4B_ERR_TOO_LARGE) when the call needs more
+    workspace than the scratch holds.  Calls that overlap on one GPU race on the scratch."""
+    if out is None:
+        raise ValueError("e4b_moe_forward_noalloc allocates nothing: pass `out`")
+    if out_f32 is True:
+        raise ValueError("e4b_moe_forward_noalloc allocates nothing: pass an out_f32 tensor or None")
+    return _moe_forward_call(_c_moe_forward_noalloc, "e4b_moe_forward_noalloc", fmt, x, w_gu, s_gu,
+                             w_dn, s_dn, topk_w, expert_offsets, sorted_slots, k, out, out_f32, None,
+                             path, stream, None, act, interleaved, b_gu, b_dn)
+

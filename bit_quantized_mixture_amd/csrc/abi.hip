@@ -35,6 +35,29 @@ int check_device() {
 
 int launched(hipError_t e) { return e == hipSuccess ? E4B_OK : E4B_ERR_HIP; }
 
+// Workspace of e4b_moe_forward_noalloc: a file-scope device array, one copy per GPU the library
+// runs on, held until the process ends.  Host code never uses the array's name as an address
+// (on the host it is only a stand-in for the symbol): the device address of the current GPU's
+// copy comes from hipGetSymbolAddress, once per device, and is kept in g_scratch.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::atomic<void*> g_scratch[kMaxDevices];
+
+int scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return E4B_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return E4B_ERR_UNSUPPORTED;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    // the address of this device's copy (the symbol lookup is idempotent, so two threads
+    // racing here store the same value)
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return E4B_ERR_HIP;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return E4B_OK;
+}
+
 int check_pack(const void* w, int64_t E, int64_t N, int64_t K, const void* o1, const void* o2,
                int64_t block) {
   if (!w || !o1 || !o2) return E4B_ERR_ARG;
@@ -289,6 +312,8 @@ const char* e4b_status_string(int status) {
     case E4B_ERR_UNSUPPORTED: return "current device is not gfx950";
     case E4B_ERR_OVERFLOW: return "size overflows the index types";
     case E4B_ERR_HIP: return "HIP runtime or launch failure";
+    case E4B_ERR_TOO_LARGE:
+      return "the call needs more workspace than the allocation-free entry point's fixed scratch";
     default: return "unknown status";
   }
 }
@@ -348,24 +373,14 @@ int e4b_moe_workspace_bytes(const e4b_moe_args* a, size_t* bytes) {
   return E4B_OK;
 }
 
-int e4b_moe_forward(const e4b_moe_args* a, void* stream) {
-  int st = check_forward_shape(a);
-  if (st != E4B_OK) return st;
-  if (a->T == 0) return check_device();  // nothing to compute; no buffer is touched
-  if (!a->x || !a->w_gu || !a->s_gu || !a->w_dn || !a->s_dn || !a->topk_w ||
-      !a->expert_offsets || !a->sorted_slots || !a->out || !a->ws)
-    return E4B_ERR_ARG;
-  const void* ptrs[] = {a->x, a->w_gu, a->s_gu, a->w_dn, a->s_dn, a->topk_w,
-                        a->expert_offsets, a->sorted_slots, a->out, a->out_f32, a->ws,
-                        a->b_gu, a->b_dn};
-  for (const void* p : ptrs)
-    if (p && !aligned16(p)) return E4B_ERR_ALIGN;
+}  // extern "C"
+
+namespace {
+
+// The forward once the workspace is known: `ws` holds at least layout_forward's total.
+int forward_impl(const e4b_moe_args* a, char* ws, hipStream_t stream) {
   FwdLayout L;
   layout_forward(a, &L);
-  if (a->ws_bytes < L.total) return E4B_ERR_WORKSPACE;
-  if ((st = check_device()) != E4B_OK) return st;
-
-  char* ws = reinterpret_cast<char*>(a->ws);
   e4b::MoeLaunch M{};
   M.fmt = a->fmt;
   M.E = a->E;
@@ -401,7 +416,57 @@ int e4b_moe_forward(const e4b_moe_args* a, void* stream) {
   M.tiles = reinterpret_cast<int32_t*>(ws + L.off_tiles);
   M.n_mtiles = reinterpret_cast<int32_t*>(ws + L.off_n);
   M.events = a->stage_events;
-  return launched(e4b::launch_moe_forward(M, (hipStream_t)stream));
+  return launched(e4b::launch_moe_forward(M, stream));
+}
+
+// Checks shared by both forward entry points, up to (not including) the workspace.
+int check_forward_call(const e4b_moe_args* a) {
+  if (!a->x || !a->w_gu || !a->s_gu || !a->w_dn || !a->s_dn || !a->topk_w ||
+      !a->expert_offsets || !a->sorted_slots || !a->out)
+    return E4B_ERR_ARG;
+  const void* ptrs[] = {a->x, a->w_gu, a->s_gu, a->w_dn, a->s_dn, a->topk_w,
+                        a->expert_offsets, a->sorted_slots, a->out, a->out_f32, a->ws,
+                        a->b_gu, a->b_dn};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return E4B_ERR_ALIGN;
+  return E4B_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int e4b_moe_forward(const e4b_moe_args* a, void* stream) {
+  int st = check_forward_shape(a);
+  if (st != E4B_OK) return st;
+  if (a->T == 0) return check_device();  // nothing to compute; no buffer is touched
+  if ((st = check_forward_call(a)) != E4B_OK) return st;
+  if (!a->ws) return E4B_ERR_ARG;
+  FwdLayout L;
+  layout_forward(a, &L);
+  if (a->ws_bytes < L.total) return E4B_ERR_WORKSPACE;
+  if ((st = check_device()) != E4B_OK) return st;
+  return forward_impl(a, reinterpret_cast<char*>(a->ws), (hipStream_t)stream);
+}
+
+size_t e4b_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int e4b_moe_forward_noalloc(const e4b_moe_args* a, void* stream) {
+  int st = check_forward_shape(a);
+  if (st != E4B_OK) return st;
+  if (a->ws || a->ws_bytes) return E4B_ERR_ARG;  // the workspace is the library's own
+  if (a->T == 0) return check_device();
+  if ((st = check_forward_call(a)) != E4B_OK) return st;
+  FwdLayout L;
+  layout_forward(a, &L);
+  if (L.total > kScratchBytes) return E4B_ERR_TOO_LARGE;
+  if ((st = check_device()) != E4B_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_ptr(&ws)) != E4B_OK) return st;
+  // Every buffer carved from the scratch is written before it is read within the call (x16,
+  // inv and tok by the conversion, the tile list and its counts by the tile builder, h and y
+  // by the two products), so nothing is cleared and the previous call's contents are harmless.
+  return forward_impl(a, reinterpret_cast<char*>(ws), (hipStream_t)stream);
 }
 
 }  // extern "C"

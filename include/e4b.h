@@ -73,7 +73,8 @@ typedef enum e4b_status {
   E4B_ERR_WORKSPACE = -4,   /* workspace missing or smaller than the queried size */
   E4B_ERR_UNSUPPORTED = -5, /* current device is not gfx950 */
   E4B_ERR_OVERFLOW = -6,    /* a count does not fit the index types (T*k >= 2^31, ...) */
-  E4B_ERR_HIP = -7          /* a HIP runtime call or kernel launch failed */
+  E4B_ERR_HIP = -7,         /* a HIP runtime call or kernel launch failed */
+  E4B_ERR_TOO_LARGE = -8    /* more workspace than e4b_moe_forward_noalloc's fixed scratch */
 } e4b_status;
 
 typedef enum e4b_fmt { E4B_FMT_NF4 = 0, E4B_FMT_MXFP4 = 1 } e4b_fmt;
@@ -202,6 +203,27 @@ int e4b_moe_workspace_bytes(const e4b_moe_args* a, size_t* bytes);
  * a fixed order, so results are deterministic run to run.
  */
 int e4b_moe_forward(const e4b_moe_args* a, void* stream);
+
+/*
+ * e4b_moe_forward_noalloc — e4b_moe_forward for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * same kernels and results; the workspace is a fixed scratch array the library holds in
+ * device memory, one copy per GPU it runs on, until the process ends
+ * (e4b_noalloc_scratch_bytes() bytes, 64 MiB: decode-sized batches, e.g. up to T = 64 tokens
+ * of a 128-expert top-8 layer with H = 2048, I = 768).
+ *   a->ws must be NULL and a->ws_bytes 0 (E4B_ERR_ARG otherwise).  A call whose workspace
+ *   (e4b_moe_workspace_bytes) exceeds the scratch returns E4B_ERR_TOO_LARGE and enqueues
+ *   nothing.  The call allocates nothing (no hipMalloc, no library allocation); the caller
+ *   passes every input and output.
+ *   Every call on one GPU shares that GPU's scratch: calls that may overlap on one GPU (on
+ *   different streams without ordering between them, or from several host threads) race and
+ *   must be serialised by the caller.  The scratch keeps the last call's contents; nothing in
+ *   it needs to start at zero.
+ */
+int e4b_moe_forward_noalloc(const e4b_moe_args* a, void* stream);
+
+/* Bytes of the scratch e4b_moe_forward_noalloc uses (a compile-time constant). */
+size_t e4b_noalloc_scratch_bytes(void);
 
 /* Arguments of e4b_grouped_dgrad. */
 typedef struct e4b_dgrad_args {

@@ -16,7 +16,7 @@ FAKE = 0x100000  # aligned, never dereferenced: every call below fails validatio
 
 def _declared():
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(e4b_\w+)\s*\(", src, re.M)))
+    return sorted(set(re.findall(r"^(?:int|size_t|const char\*)\s+(e4b_\w+)\s*\(", src, re.M)))
 
 
 def test_header_declares_the_entry_points():
@@ -24,7 +24,8 @@ def test_header_declares_the_entry_points():
     for n in ("e4b_pack_nf4", "e4b_pack_mxfp4", "e4b_route_permute", "e4b_moe_forward",
               "e4b_route_workspace_bytes", "e4b_moe_workspace_bytes", "e4b_status_string", "e4b_version",
               "e4b_dgrad_workspace_bytes", "e4b_grouped_dgrad", "e4b_pack_int4_b32",
-              "e4b_quantize_act_int8", "e4b_int4_gemv_workspace_bytes", "e4b_gemv_int4_b32"):
+              "e4b_quantize_act_int8", "e4b_int4_gemv_workspace_bytes", "e4b_gemv_int4_b32",
+              "e4b_moe_forward_noalloc", "e4b_noalloc_scratch_bytes"):
         assert n in names
 
 
@@ -121,6 +122,19 @@ def test_forward_rejects_bad_arguments(e4b):
     assert f(T=1 << 28, k=8) == ERR_OVERFLOW
     assert f(T=1 << 20, H=1 << 12) == ERR_OVERFLOW
     assert f(T=1, H=1 << 16, I=1 << 15) == ERR_OVERFLOW   # one expert's stack >= 2^31 bytes
+
+
+def test_noalloc_forward_rejects_bad_arguments(e4b):
+    """The allocation-free forward: same argument checks, no workspace argument, and a call that
+    needs more than the fixed scratch is refused (all before any device is touched)."""
+    f = lambda **kw: e4b._c_moe_forward_noalloc(ctypes.byref(_args(e4b, **kw)), None)
+    assert e4b.e4b_noalloc_scratch_bytes() == 64 << 20
+    assert f() == ERR_ARG                            # a workspace pointer is given
+    assert f(ws=None, ws_bytes=0, fmt=2) == ERR_ARG
+    assert f(ws=None, ws_bytes=0, H=96) == ERR_SHAPE
+    assert f(ws=None, ws_bytes=0, out=FAKE + 2) == ERR_ALIGN
+    assert f(ws=None, ws_bytes=0, T=1 << 16, k=8) == -8    # E4B_ERR_TOO_LARGE
+    assert e4b.e4b_status_string(-8).startswith("the call needs more workspace")
 
 
 def test_workspace_sizes_cover_the_intermediates(e4b):
