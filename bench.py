@@ -18,8 +18,9 @@ CPU-oracle baseline timed on a bounded sample of the headline workload.  Also un
 "secondary": the grouped dgrad on the Mixtral-shaped layer's packed down and gate_up stacks
 with its own routing, and the int4-b32 routed decode GEMV (exact integer accumulation) on the
 decode layer's gate_up stack at T = 64 and 1 and on one dense [14336, 4096] matrix at M = 1, in
-GB/s of weight streaming.  "hbm_ceiling" holds the rate of a plain device copy and of a plain
-streaming read measured in the same run, beside the published 8 TB/s.
+GB/s of weight streaming.  "hbm_ceiling" holds the rates of a plain streaming read and a plain
+copy (the library's e4b_stream_probe) and of torch's device copy, measured in the same run,
+beside the published 8 TB/s.
 """
 from __future__ import annotations
 
@@ -416,14 +417,17 @@ def int4_report(torch, e4b, wl, T: int, steps: int, warmup: int) -> dict:
             "algorithmic_bytes": nbytes, "achieved_gbs": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS}
 
 
-def hbm_ceiling(torch, nbytes: int = 2 << 30, reps: int = 10) -> dict:
-    """Measured ceilings beside the published HBM peak: a plain device-to-device copy of
-    `nbytes` (read + written bytes per second) and a plain streaming read (a sum over the same
-    buffer), each the mean of `reps` launches timed with HIP events on the current stream."""
+def hbm_ceiling(torch, e4b, nbytes: int = 4 << 30, reps: int = 10) -> dict:
+    """Measured ceilings beside the published HBM peak, on a buffer of `nbytes` (16 times the
+    256 MB Infinity Cache): the library's plain streaming read (e4b_stream_probe, 16-byte loads,
+    nothing written) and plain copy (read + written bytes per second), and torch's device copy;
+    each the mean of `reps` launches timed with HIP events on the current stream."""
     a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
     b = torch.empty_like(a)
     res = {}
-    for key, fn, moved in (("copy_gbs", lambda: b.copy_(a), 2 * nbytes), ("read_gbs", lambda: a.sum(), nbytes)):
+    for key, fn, moved in (("read_gbs", lambda: e4b.e4b_stream_probe(a), nbytes),
+                           ("copy_gbs", lambda: e4b.e4b_stream_probe(a, b), 2 * nbytes),
+                           ("torch_copy_gbs", lambda: b.copy_(a), 2 * nbytes)):
         fn()
         torch.cuda.synchronize()
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -489,8 +493,9 @@ def main():
         {"dgrad", "prefill", "int4", "decode"} if args.secondary == "all" else set(args.secondary.split(",")))
     del layer
     torch.cuda.empty_cache()
-    ceiling = hbm_ceiling(torch)
-    log(f"[bench] HBM ceiling: copy {ceiling['copy_gbs']:.0f} GB/s, read {ceiling['read_gbs']:.0f} GB/s")
+    ceiling = hbm_ceiling(torch, e4b)
+    log(f"[bench] HBM ceiling: read {ceiling['read_gbs']:.0f} GB/s, copy {ceiling['copy_gbs']:.0f} GB/s "
+        f"(torch copy {ceiling['torch_copy_gbs']:.0f} GB/s)")
 
     dgrad_on = "mixtral_nf4_prefill"
     for name in ("mixtral_nf4_prefill", "skewed_nf4_prefill", "mxfp4_moe"):

@@ -16,7 +16,7 @@ __all__ = [
     "E4BError", "E4B_FMT_NF4", "E4B_FMT_MXFP4", "E4B_PATH_AUTO", "E4B_PATH_GEMM", "E4B_PATH_GEMV",
     "E4B_ROUTE_RENORMALIZE", "E4B_ACT_CLAMPED_GLU", "E4B_GU_INTERLEAVED", "lib_path", "e4b_version", "e4b_status_string", "e4b_pack_nf4",
     "e4b_pack_mxfp4", "e4b_route_workspace_bytes", "e4b_route_permute", "e4b_moe_workspace_bytes",
-    "e4b_moe_forward", "e4b_moe_forward_noalloc", "e4b_noalloc_scratch_bytes", "MoeArgs", "e4b_dgrad_workspace_bytes", "e4b_grouped_dgrad", "DgradArgs",
+    "e4b_moe_forward", "e4b_moe_forward_noalloc", "e4b_noalloc_scratch_bytes", "e4b_stream_probe", "MoeArgs", "e4b_dgrad_workspace_bytes", "e4b_grouped_dgrad", "DgradArgs",
 ]
 
 E4B_FMT_NF4, E4B_FMT_MXFP4 = 0, 1
@@ -84,6 +84,7 @@ _c_moe_ws = _decl("e4b_moe_workspace_bytes", [ctypes.POINTER(MoeArgs), ctypes.PO
 _c_moe_forward = _decl("e4b_moe_forward", [ctypes.POINTER(MoeArgs), _vp])
 _c_moe_forward_noalloc = _decl("e4b_moe_forward_noalloc", [ctypes.POINTER(MoeArgs), _vp])
 _c_noalloc_bytes = _decl("e4b_noalloc_scratch_bytes", [], _sz)
+_c_stream_probe = _decl("e4b_stream_probe", [_vp, _vp, _i64, _i32, _vp])
 _c_dgrad_ws = _decl("e4b_dgrad_workspace_bytes", [ctypes.POINTER(DgradArgs), ctypes.POINTER(_sz)])
 _c_dgrad = _decl("e4b_grouped_dgrad", [ctypes.POINTER(DgradArgs), _vp])
 _c_pack_int4 = _decl("e4b_pack_int4_b32", [_vp, _i64, _i64, _i64, _vp, _vp, _vp])
@@ -504,3 +505,15 @@ def e4b_moe_forward_noalloc(fmt, x, w_gu, s_gu, w_dn, s_dn, topk_w, expert_offse
                              w_dn, s_dn, topk_w, expert_offsets, sorted_slots, k, out, out_f32, None,
                              path, stream, None, act, interleaved, b_gu, b_dn)
 
+
+def e4b_stream_probe(src, dst=None, stream=None):
+    """Plain streaming read of `src` (dst None) or copy src -> dst: the measured memory ceiling
+    beside the layer's rates.  Tensors must be contiguous device tensors of equal byte size."""
+    _need(src, "src", (src.dtype,))
+    nbytes = src.numel() * src.element_size()
+    if dst is not None:
+        _need(dst, "dst", (dst.dtype,), device=src.device)
+        if dst.numel() * dst.element_size() != nbytes:
+            raise ValueError("dst must have the byte size of src")
+    _check("e4b_stream_probe", _c_stream_probe(_ptr(src), _ptr(dst), nbytes, 0 if dst is None else 1,
+                                               _stream(stream)))

@@ -451,6 +451,19 @@ int e4b_moe_forward(const e4b_moe_args* a, void* stream) {
 
 size_t e4b_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
+int e4b_stream_probe(const void* src, void* dst, int64_t bytes, int32_t mode, void* stream) {
+  if (!src || bytes <= 0 || (mode != 0 && mode != 1) || (mode == 1 && !dst)) return E4B_ERR_ARG;
+  if (bytes % 16) return E4B_ERR_SHAPE;
+  if (!aligned16(src) || (dst && !aligned16(dst))) return E4B_ERR_ALIGN;
+  int st = check_device();
+  if (st != E4B_OK) return st;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return E4B_ERR_HIP;
+  return launched(e4b::launch_stream_probe(src, dst, bytes, mode, cus, (hipStream_t)stream));
+}
+
 int e4b_moe_forward_noalloc(const e4b_moe_args* a, void* stream) {
   int st = check_forward_shape(a);
   if (st != E4B_OK) return st;

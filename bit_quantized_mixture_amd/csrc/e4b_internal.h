@@ -117,4 +117,9 @@ hipError_t launch_gemv(const MoeLaunch& L, hipStream_t stream, int stage);
 // The same kernels over the tail tiles of the MFMA-tile path (its activation order).
 hipError_t launch_gemv_tails(const MoeLaunch& L, hipStream_t stream, int stage);
 
+// Streaming read (mode 0; dst: NULL or a 4-byte sink that is never written in practice) or
+// copy (mode 1) of `bytes` (a multiple of 16) with cus * 8 workgroups.
+hipError_t launch_stream_probe(const void* src, void* dst, int64_t bytes, int mode, int cus,
+                               hipStream_t stream);
+
 }  // namespace e4b

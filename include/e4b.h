@@ -314,6 +314,18 @@ int e4b_int4_gemv_workspace_bytes(const e4b_int4_gemv_args* a, size_t* bytes);
  */
 int e4b_gemv_int4_b32(const e4b_int4_gemv_args* a, void* stream);
 
+/*
+ * e4b_stream_probe — a plain streaming read (mode 0) or copy (mode 1) of `bytes` bytes, the
+ * memory ceiling the layer's HBM rates are read against on the same device (grouped-nf4-gemm
+ * 0.25.0 project description, "See it on your own hardware first": a ratio is shown beside
+ * its instrument's own reference).  Not part of the layer.
+ *   src   device buffer of `bytes` bytes (a multiple of 16), read once with 16-byte loads.
+ *   dst   mode 1: device buffer of `bytes` bytes, written with the copy.  mode 0: NULL, or a
+ *         4-byte word the read kernel never writes in practice (its loads feed a value it
+ *         stores only on an impossible match).
+ */
+int e4b_stream_probe(const void* src, void* dst, int64_t bytes, int32_t mode, void* stream);
+
 /* Static description of a status code. */
 const char* e4b_status_string(int status);
 
