@@ -13,7 +13,8 @@ carries, under "secondary", the Mixtral-shaped NF4 prefill layer (E=8, H=4096, I
 T=4096), the MXFP4 layer (also run as the MXFP4 family's expert variant: interleaved gate/up
 rows, clamped GLU, per-expert biases) and the 128-expert decode layer at T = 64, 16, 4, 1 (warm,
 and cold with the 256 MB Infinity Cache flushed by reading 1 GiB before every step; eager
-launches with per-stage HIP events, and the same step replayed from a HIP graph), and a float64
+launches with per-stage HIP events, and the same step replayed from a HIP graph; at T = 1, 4, 8
+also the single-launch decode step, eager and graph-replayed), and a float64
 CPU-oracle baseline timed on a bounded sample of the headline workload.  Also under
 "secondary": the grouped dgrad on the Mixtral-shaped layer's packed down and gate_up stacks
 with its own routing, and the int4-b32 routed decode GEMV (exact integer accumulation) on the
@@ -417,6 +418,61 @@ def int4_report(torch, e4b, wl, T: int, steps: int, warmup: int) -> dict:
             "algorithmic_bytes": nbytes, "achieved_gbs": gbs, "frac_of_hbm_peak": gbs / PEAK_HBM_GBS}
 
 
+def decode_step_report(torch, layer: Layer, T: int, steps: int, warmup: int) -> dict:
+    """The single-launch decode step (e4b_moe_decode_step: routing, gate_up, down and combine in
+    one kernel) on the layer's packed weights at batch T, eager (HIP events on the current
+    stream around each call) and replayed from a HIP graph.  Algorithmic bytes: the active
+    experts' packed weights and scales, x, logits and the bf16 output."""
+    e4b, wl = layer.e4b, layer.wl.with_T(T)
+    dev = "cuda:0"
+    x = torch.from_numpy(make_x(wl).view(np.int16)).to(dev).view(torch.bfloat16)
+    logits = torch.from_numpy(make_logits(wl)).to(dev)
+    ws = torch.zeros(e4b.e4b_decode_workspace_bytes(wl.fmt, wl.E, wl.H, wl.I, T, wl.k), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, wl.H), dtype=torch.bfloat16, device=dev)
+    gp, gs = layer.packed["gate_up"]
+    dp, ds = layer.packed["down"]
+    run = lambda: e4b.e4b_moe_decode_step(wl.fmt, logits, x, gp, gs, dp, ds, wl.k, out=out, ws=ws)
+    ids = np.argsort(-make_logits(wl), axis=1, kind="stable")[:, :wl.k]
+    active = len(np.unique(ids))
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    gc.collect()
+    gc.disable()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    gc.enable()
+    eager = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(steps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    graph = t0.elapsed_time(t1) / steps
+    del g
+    nbytes = active * 3 * wl.H * wl.I * bytes_per_weight(wl.fmt) + 2 * T * wl.H * 2 + 4 * T * wl.E
+    return {"T": T, "active_experts": active, "ms_per_step": eager, "graph_ms_per_step": graph,
+            "tokens_per_s": T / (eager / 1e3), "graph_tokens_per_s": T / (graph / 1e3),
+            "algorithmic_bytes": nbytes, "achieved_gbs": nbytes / (eager / 1e3) / 1e9,
+            "frac_of_hbm_peak": nbytes / (eager / 1e3) / 1e9 / PEAK_HBM_GBS}
+
+
 def hbm_ceiling(torch, e4b, nbytes: int = 4 << 30, reps: int = 10) -> dict:
     """Measured ceilings beside the published HBM peak, on a buffer of `nbytes` (16 times the
     256 MB Infinity Cache): the library's plain streaming read (e4b_stream_probe, 16-byte loads,
@@ -540,6 +596,11 @@ def main():
             secondary[key] = batch_report(torch, lay, T, max(args.steps, 50), args.warmup, flush,
                                           graph=not flush)
             log(fmt_rep(key, secondary[key]))
+        for T in (1, 4, 8):
+            key = f"{dwl.name}_T{T}_single_launch"
+            secondary[key] = r = decode_step_report(torch, lay, T, max(args.steps, 50), args.warmup)
+            log(f"[bench] {key}: {r['ms_per_step']:.4f} ms/step eager, {r['graph_ms_per_step']:.4f} ms/step "
+                f"graph, {r['achieved_gbs']:.0f} GB/s ({100 * r['frac_of_hbm_peak']:.1f}% of HBM peak)")
         del lay
         torch.cuda.empty_cache()
 

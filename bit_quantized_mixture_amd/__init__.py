@@ -16,7 +16,7 @@ __all__ = [
     "E4BError", "E4B_FMT_NF4", "E4B_FMT_MXFP4", "E4B_PATH_AUTO", "E4B_PATH_GEMM", "E4B_PATH_GEMV",
     "E4B_ROUTE_RENORMALIZE", "E4B_ACT_CLAMPED_GLU", "E4B_GU_INTERLEAVED", "lib_path", "e4b_version", "e4b_status_string", "e4b_pack_nf4",
     "e4b_pack_mxfp4", "e4b_route_workspace_bytes", "e4b_route_permute", "e4b_moe_workspace_bytes",
-    "e4b_moe_forward", "e4b_moe_forward_noalloc", "e4b_noalloc_scratch_bytes", "e4b_stream_probe", "MoeArgs", "e4b_dgrad_workspace_bytes", "e4b_grouped_dgrad", "DgradArgs",
+    "e4b_moe_forward", "e4b_moe_forward_noalloc", "e4b_noalloc_scratch_bytes", "e4b_stream_probe", "e4b_decode_workspace_bytes", "e4b_moe_decode_step", "MoeArgs", "e4b_dgrad_workspace_bytes", "e4b_grouped_dgrad", "DgradArgs",
 ]
 
 E4B_FMT_NF4, E4B_FMT_MXFP4 = 0, 1
@@ -46,6 +46,18 @@ class MoeArgs(ctypes.Structure):
         ("out", _vp), ("out_f32", _vp), ("ws", _vp), ("ws_bytes", _sz),
         ("flags", _i32), ("reserved", _i32), ("stage_events", ctypes.POINTER(_vp)),
         ("b_gu", _vp), ("b_dn", _vp),
+    ]
+
+
+class DecodeArgs(ctypes.Structure):
+    """Mirror of struct e4b_decode_args."""
+    _fields_ = [
+        ("fmt", _i32), ("k", _i32), ("E", _i64), ("H", _i64), ("I", _i64), ("T", _i64),
+        ("route_flags", _i32), ("flags", _i32),
+        ("logits", _vp), ("x", _vp), ("w_gu", _vp), ("s_gu", _vp), ("w_dn", _vp), ("s_dn", _vp),
+        ("b_gu", _vp), ("b_dn", _vp), ("topk_ids", _vp), ("topk_w", _vp), ("expert_offsets", _vp),
+        ("sorted_slots", _vp), ("out", _vp), ("out_f32", _vp), ("status", _vp),
+        ("spin_limit", _i32), ("reserved", _i32), ("ws", _vp), ("ws_bytes", _sz),
     ]
 
 
@@ -85,6 +97,8 @@ _c_moe_forward = _decl("e4b_moe_forward", [ctypes.POINTER(MoeArgs), _vp])
 _c_moe_forward_noalloc = _decl("e4b_moe_forward_noalloc", [ctypes.POINTER(MoeArgs), _vp])
 _c_noalloc_bytes = _decl("e4b_noalloc_scratch_bytes", [], _sz)
 _c_stream_probe = _decl("e4b_stream_probe", [_vp, _vp, _i64, _i32, _vp])
+_c_decode_ws = _decl("e4b_decode_workspace_bytes", [ctypes.POINTER(DecodeArgs), ctypes.POINTER(_sz)])
+_c_decode_step = _decl("e4b_moe_decode_step", [ctypes.POINTER(DecodeArgs), _vp])
 _c_dgrad_ws = _decl("e4b_dgrad_workspace_bytes", [ctypes.POINTER(DgradArgs), ctypes.POINTER(_sz)])
 _c_dgrad = _decl("e4b_grouped_dgrad", [ctypes.POINTER(DgradArgs), _vp])
 _c_pack_int4 = _decl("e4b_pack_int4_b32", [_vp, _i64, _i64, _i64, _vp, _vp, _vp])
@@ -517,3 +531,101 @@ def e4b_stream_probe(src, dst=None, stream=None):
             raise ValueError("dst must have the byte size of src")
     _check("e4b_stream_probe", _c_stream_probe(_ptr(src), _ptr(dst), nbytes, 0 if dst is None else 1,
                                                _stream(stream)))
+
+
+def _decode_args(fmt, E, H, I, T, k) -> DecodeArgs:
+    a = DecodeArgs()
+    a.fmt, a.k, a.E, a.H, a.I, a.T = _FMT[fmt], k, E, H, I, T
+    return a
+
+
+def e4b_decode_workspace_bytes(fmt, E: int, H: int, I: int, T: int, k: int) -> int:
+    n = _sz(0)
+    _check("e4b_decode_workspace_bytes",
+           _c_decode_ws(ctypes.byref(_decode_args(fmt, E, H, I, T, k)), ctypes.byref(n)))
+    return n.value
+
+
+def e4b_moe_decode_step(fmt, logits, x, w_gu, s_gu, w_dn, s_dn, k: int, renormalize: bool = True,
+                        out=None, out_f32=None, ws=None, route_out=None, status=None,
+                        spin_limit: int = 0, act: str = "swiglu", interleaved: bool = False,
+                        b_gu=None, b_dn=None, stream=None):
+    """Routing + expert layer for T <= 8 tokens in one launch.  Returns (out, out_f32, route)
+    where route is (topk_ids, topk_w, expert_offsets, sorted_slots) or None.
+
+    `out_f32`: True to allocate, a tensor, or None.  `route_out`: True to allocate the routing
+    outputs, a 4-tuple of tensors to fill, or None.  `ws`: a uint8 device tensor of at least
+    e4b_decode_workspace_bytes(), zero-filled before its first use (allocated
+    here with zeros when not given); keep it for later calls.  `status`: an int32 [1] device
+    tensor that receives 0, or 1 if the kernel's grid barrier gave up waiting.
+    """
+    if fmt not in _FMT:
+        raise ValueError(f"fmt must be 'nf4' or 'mxfp4', not {fmt!r}")
+    f = _FMT[fmt]
+    _need(x, "x", _BF16)
+    dev = x.device
+    if x.dim() != 2:
+        raise ValueError(f"x must be [T, H], got shape {tuple(x.shape)}")
+    T, H = x.shape
+    _need(logits, "logits", (torch.float32,), device=dev)
+    if logits.dim() != 2 or logits.shape[0] != T:
+        raise ValueError(f"logits must be [T, E] with T = {T}, got shape {tuple(logits.shape)}")
+    E = logits.shape[1]
+    _need(w_dn, "w_dn", (torch.uint8,), device=dev)
+    if f == E4B_FMT_NF4 and w_dn.dim() == 3:
+        I = w_dn.shape[2] * 2
+    elif f == E4B_FMT_MXFP4 and w_dn.dim() == 4 and w_dn.shape[3] == 16:
+        I = w_dn.shape[2] * 32
+    else:
+        raise ValueError(f"w_dn of shape {tuple(w_dn.shape)} is not a {fmt} down stack")
+    for name, t, (N, K) in (("gate_up", (w_gu, s_gu), (2 * I, H)), ("down", (w_dn, s_dn), (H, I))):
+        cs, cd, ss, sd = _stack_shapes(f, E, N, K)
+        _need(t[0], f"w_{name}", (cd,), cs, dev)
+        _need(t[1], f"s_{name}", (sd,), ss, dev)
+    for name, b, n in (("b_gu", b_gu, (E, 2 * I)), ("b_dn", b_dn, (E, H))):
+        if b is not None:
+            _need(b, name, (torch.float32,), n, dev)
+    if act not in ("swiglu", "clamped_glu"):
+        raise ValueError(f"act must be 'swiglu' or 'clamped_glu', not {act!r}")
+    with _on_stream(stream) as st:
+        if out is None:
+            out = st.alloc((T, H), dtype=torch.bfloat16, device=dev)
+        if out_f32 is True:
+            out_f32 = st.alloc((T, H), dtype=torch.float32, device=dev)
+        if route_out is True:
+            route_out = (st.alloc((T, k), dtype=torch.int32, device=dev),
+                         st.alloc((T, k), dtype=torch.float32, device=dev),
+                         st.alloc((E + 1,), dtype=torch.int32, device=dev),
+                         st.alloc((T * k,), dtype=torch.int32, device=dev))
+        if ws is None:
+            if st.ctx is False:
+                st.alloc(0)  # raises: a raw foreign stream needs a caller workspace
+            ws = torch.zeros((max(e4b_decode_workspace_bytes(fmt, E, H, I, T, k), 256),),
+                             dtype=torch.uint8, device=dev)
+    _need(out, "out", _BF16, (T, H), dev)
+    if out_f32 is not None:
+        _need(out_f32, "out_f32", (torch.float32,), (T, H), dev)
+    if route_out is not None:
+        for name, t, dt, shp in zip(("topk_ids", "topk_w", "expert_offsets", "sorted_slots"), route_out,
+                                    (torch.int32, torch.float32, torch.int32, torch.int32),
+                                    ((T, k), (T, k), (E + 1,), (T * k,))):
+            _need(t, name, (dt,), shp, dev)
+    if status is not None:
+        _need(status, "status", (torch.int32,), (1,), dev)
+    _need(ws, "ws", (torch.uint8,), device=dev)
+    a = _decode_args(fmt, E, H, I, T, k)
+    a.route_flags = E4B_ROUTE_RENORMALIZE if renormalize else 0
+    a.flags = (E4B_ACT_CLAMPED_GLU if act == "clamped_glu" else 0) | (E4B_GU_INTERLEAVED if interleaved else 0)
+    a.logits, a.x = logits.data_ptr(), x.data_ptr()
+    a.w_gu, a.s_gu, a.w_dn, a.s_dn = w_gu.data_ptr(), s_gu.data_ptr(), w_dn.data_ptr(), s_dn.data_ptr()
+    a.b_gu = None if b_gu is None else b_gu.data_ptr()
+    a.b_dn = None if b_dn is None else b_dn.data_ptr()
+    if route_out is not None:
+        a.topk_ids, a.topk_w, a.expert_offsets, a.sorted_slots = (t.data_ptr() for t in route_out)
+    a.out = out.data_ptr()
+    a.out_f32 = None if out_f32 is None else out_f32.data_ptr()
+    a.status = None if status is None else status.data_ptr()
+    a.spin_limit = spin_limit
+    a.ws, a.ws_bytes = ws.data_ptr(), ws.numel() * ws.element_size()
+    _check("e4b_moe_decode_step", _c_decode_step(ctypes.byref(a), _stream(stream)))
+    return out, out_f32, route_out

@@ -149,6 +149,21 @@ int check_forward_shape(const e4b_moe_args* a) {
   return E4B_OK;
 }
 
+int check_decode(const e4b_decode_args* a) {
+  if (!a) return E4B_ERR_ARG;
+  if (a->fmt != E4B_FMT_NF4 && a->fmt != E4B_FMT_MXFP4) return E4B_ERR_ARG;
+  if (a->reserved != 0) return E4B_ERR_ARG;
+  if ((a->route_flags & ~E4B_ROUTE_RENORMALIZE) != 0) return E4B_ERR_ARG;
+  if ((a->flags & ~(E4B_ACT_CLAMPED_GLU | E4B_GU_INTERLEAVED)) != 0) return E4B_ERR_ARG;
+  if (a->E <= 0 || a->H <= 0 || a->I <= 0 || a->k < 1 || a->k > a->E) return E4B_ERR_ARG;
+  if (a->T < 1 || a->T > 8 || a->T * a->k > 64 || a->E > 1024) return E4B_ERR_SHAPE;
+  if (a->T * a->H > 32768) return E4B_ERR_SHAPE;  // x is held in LDS: at most 64 KB
+  if (a->H % 64 || a->I % 64) return E4B_ERR_SHAPE;
+  if (a->I * a->H >= (int64_t(1) << 31) || a->H >= (int64_t(1) << 24) || a->I >= (int64_t(1) << 24))
+    return E4B_ERR_OVERFLOW;
+  return E4B_OK;
+}
+
 int dgrad_check(const e4b_dgrad_args* a, int64_t* max_tiles) {
   if (!a) return E4B_ERR_ARG;
   if (a->fmt != E4B_FMT_NF4 && a->fmt != E4B_FMT_MXFP4) return E4B_ERR_ARG;
@@ -447,6 +462,64 @@ int e4b_moe_forward(const e4b_moe_args* a, void* stream) {
   if (a->ws_bytes < L.total) return E4B_ERR_WORKSPACE;
   if ((st = check_device()) != E4B_OK) return st;
   return forward_impl(a, reinterpret_cast<char*>(a->ws), (hipStream_t)stream);
+}
+
+int e4b_decode_workspace_bytes(const e4b_decode_args* a, size_t* bytes) {
+  if (!bytes) return E4B_ERR_ARG;
+  const int st = check_decode(a);
+  if (st != E4B_OK) return st;
+  *bytes = e4b::decode_ctl_bytes(a->H) + align_up(size_t(a->T * a->k) * size_t(a->I) * 2) +
+           align_up(size_t((a->H + 15) / 16) * 8 * 8 * 16 * 4);
+  return E4B_OK;
+}
+
+int e4b_moe_decode_step(const e4b_decode_args* a, void* stream) {
+  int st = check_decode(a);
+  if (st != E4B_OK) return st;
+  if (!a->logits || !a->x || !a->w_gu || !a->s_gu || !a->w_dn || !a->s_dn || !a->out || !a->ws)
+    return E4B_ERR_ARG;
+  if ((a->topk_ids == nullptr) != (a->topk_w == nullptr)) return E4B_ERR_ARG;
+  const void* ptrs[] = {a->logits, a->x, a->w_gu, a->s_gu, a->w_dn, a->s_dn, a->b_gu, a->b_dn,
+                        a->topk_ids, a->topk_w, a->expert_offsets, a->sorted_slots, a->out,
+                        a->out_f32, a->ws};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return E4B_ERR_ALIGN;
+  size_t need = 0;
+  e4b_decode_workspace_bytes(a, &need);
+  if (a->ws_bytes < need) return E4B_ERR_WORKSPACE;
+  if ((st = check_device()) != E4B_OK) return st;
+  char* ws = reinterpret_cast<char*>(a->ws);
+  e4b::DecodeLaunch L{};
+  L.fmt = a->fmt;
+  L.E = a->E;
+  L.H = a->H;
+  L.I = a->I;
+  L.T = a->T;
+  L.k = a->k;
+  L.renorm = (a->route_flags & E4B_ROUTE_RENORMALIZE) ? 1 : 0;
+  L.clamped_glu = (a->flags & E4B_ACT_CLAMPED_GLU) ? 1 : 0;
+  L.interleaved = (a->flags & E4B_GU_INTERLEAVED) ? 1 : 0;
+  L.spin_limit = a->spin_limit == 0 ? (1 << 20) : a->spin_limit;
+  L.logits = a->logits;
+  L.x = a->x;
+  L.w_gu = a->w_gu;
+  L.s_gu = a->s_gu;
+  L.w_dn = a->w_dn;
+  L.s_dn = a->s_dn;
+  L.b_gu = a->b_gu;
+  L.b_dn = a->b_dn;
+  L.ids = a->topk_ids;
+  L.w = a->topk_w;
+  L.offsets = a->expert_offsets;
+  L.slots = a->sorted_slots;
+  L.out = a->out;
+  L.out_f32 = a->out_f32;
+  L.status = a->status;
+  const size_t ctl = e4b::decode_ctl_bytes(a->H);
+  L.ctl = reinterpret_cast<uint32_t*>(ws);
+  L.h = reinterpret_cast<_Float16*>(ws + ctl);
+  L.part = reinterpret_cast<float*>(ws + ctl + align_up(size_t(a->T * a->k) * size_t(a->I) * 2));
+  return launched(e4b::launch_decode_step(L, (hipStream_t)stream));
 }
 
 size_t e4b_noalloc_scratch_bytes(void) { return kScratchBytes; }

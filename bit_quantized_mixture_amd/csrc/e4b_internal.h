@@ -117,6 +117,36 @@ hipError_t launch_gemv(const MoeLaunch& L, hipStream_t stream, int stage);
 // The same kernels over the tail tiles of the MFMA-tile path (its activation order).
 hipError_t launch_gemv_tails(const MoeLaunch& L, hipStream_t stream, int stage);
 
+// Single-launch decode step (T <= 8, T*k <= 64): routing, gate_up + activation, down and the
+// weighted combine in one kernel with one grid barrier.
+struct DecodeLaunch {
+  int fmt;
+  int64_t E, H, I, T;
+  int k;
+  int renorm, clamped_glu, interleaved;
+  int spin_limit;
+  const float* logits;
+  const uint16_t* x;
+  const uint8_t* w_gu;
+  const void* s_gu;
+  const uint8_t* w_dn;
+  const void* s_dn;
+  const float* b_gu;
+  const float* b_dn;
+  int32_t* ids;       // nullable outputs
+  float* w;
+  int32_t* offsets;
+  int32_t* slots;
+  uint16_t* out;
+  float* out_f32;     // nullable
+  _Float16* h;        // workspace [T*k, I]
+  float* part;        // workspace [ceil(H/16)][8][8][16] column-block sums
+  uint32_t* ctl;      // workspace control words (decode_ctl_bytes), zero between calls
+  int32_t* status;    // nullable
+};
+size_t decode_ctl_bytes(int64_t H);
+hipError_t launch_decode_step(const DecodeLaunch& L, hipStream_t stream);
+
 // Streaming read (mode 0; dst: NULL or a 4-byte sink that is never written in practice) or
 // copy (mode 1) of `bytes` (a multiple of 16) with cus * 8 workgroups.
 hipError_t launch_stream_probe(const void* src, void* dst, int64_t bytes, int mode, int cus,

@@ -38,6 +38,7 @@
 
 #include "e4b_device.h"
 #include "e4b_internal.h"
+#include "e4b_topk.h"
 
 namespace e4b {
 
@@ -540,6 +541,536 @@ __global__ void __launch_bounds__(kThreads)
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Single-launch decode step for a few tokens (T <= 8, T*k <= 64): the router epilogue, the
+// gate_up products with the activation, the down products and the weighted combine in one
+// kernel (grouped-nf4-gemm 0.25.0 project description, "What is measured", limit 1: at
+// decode the launches, not the bytes, set the time).
+//
+// * Routing: every workgroup computes the top-k of the T tokens itself (one wave per token,
+//   the router's own per-token routine, so ids and weights are bit-identical to
+//   e4b_route_permute), sorts the T*k slots expert-major (token-ascending inside an expert)
+//   and lists the active experts as tiles of <= T rows.  Workgroup 0 writes the routing out.
+// * gate_up: a work item is (tile, 8 gate + 8 up rows); its K steps are split over the 8
+//   waves and added in LDS in wave order; the activation goes to h (fp16, sorted-row order)
+//   in the workspace with device-coherent stores (written through to memory, so no cache
+//   write-back is needed before other workgroups read it).  x is converted from bf16 to fp16
+//   as it is loaded.
+// * One grid barrier: workgroups arrive on 8 group counters (blockIdx % 8, one cache line
+//   each); the last of a group arrives on a top counter, the last of all raises the 8 group
+//   flags that the workgroups poll.  Polls are bounded: a wait that gives up sets a flag
+//   reported through `status`, and every workgroup still runs to the end.  The first down
+//   weights of each wave are loaded while the barrier is pending.
+// * down + combine: a work item is (16 output columns, a group of tiles); its (tile, K step)
+//   units are spread over the 8 waves, each weighting its product rows by the slot's routing
+//   weight into per-token sums, added over lanes and waves in a fixed order.  Items of the
+//   same columns store their sums (device-coherent) and count themselves on a per-column
+//   counter; the last adds the groups' sums in group order and writes the output.  No y
+//   buffer, no second grid barrier, deterministic.
+// * Exit: the last workgroup to finish resets the barrier words (the column counters are
+//   reset by their last users), so the next call on the same workspace starts from zero.
+
+constexpr int kDecMaxT = 8;    // tokens
+constexpr int kDecMaxS = 64;   // routed slots (one wave holds them)
+constexpr int kDecGroups = 8;  // barrier groups
+constexpr int kDecXChunks = 8; // 16-byte chunks of x per thread: T * H <= 8 * 8 * 512
+constexpr int kDecMaxTG = 8;   // tile groups per column block in the down phase
+// control words (uint32 offsets): group counters and flags one 64-byte line apart
+constexpr int kCtlGrp = 0, kCtlGo = 128, kCtlTop = 256, kCtlDepart = 272, kCtlGaveUp = 288,
+              kCtlCols = 512;
+
+struct DecodeStepArgs {
+  int32_t E, H, I, T, k, renorm;
+  int32_t clamped_glu, interleaved;
+  int32_t spin_limit;          // barrier polls before giving up (negative: do not wait)
+  const float* logits;         // [T, E]
+  const uint16_t* x;           // [T, H] bf16
+  const uint8_t* w_gu;
+  const void* s_gu;
+  const uint8_t* w_dn;
+  const void* s_dn;
+  const float* b_gu;           // nullable [E, 2I]
+  const float* b_dn;           // nullable [E, H]
+  int32_t* ids_out;            // nullable [T, k]
+  float* w_out;                // nullable [T, k]
+  int32_t* offsets_out;        // nullable [E + 1]
+  int32_t* slots_out;          // nullable [T * k]
+  uint16_t* out;               // [T, H] bf16
+  float* out_f32;              // nullable [T, H]
+  _Float16* h;                 // workspace [T * k, I], sorted-row order
+  float* part;                 // workspace [H / 16][kDecMaxTG][kDecMaxT][16] column-block sums
+  uint32_t* ctl;               // workspace control words (zero between calls)
+  int32_t* status;             // nullable: 0, or 1 when a barrier wait gave up
+};
+
+constexpr int kCohere = 16;  // buffer cache policy: device-coherent (sc1) load / store
+
+// 8 bf16 (one 16-byte load) -> 8 fp16, round to nearest even (exact in fp16's normal range).
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 raw) {
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const _Float16 lo = (_Float16)__uint_as_float(raw[i] << 16);
+    const _Float16 hi = (_Float16)__uint_as_float(raw[i] & 0xFFFF0000u);
+    o[i] = uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
+  }
+  return o;
+}
+
+// One 256-wide K step of a 16-row weight block against <= 16 activation rows (the MFMA
+// layout of moe_gemv_ks_kernel): acc[q & 1] += W[16 rows, kstep..] . A[cols, kstep..].
+// `act` holds the lane's 8 activation chunks of the step in natural order (fp16).
+template <int FMT>
+__device__ __forceinline__ void decode_step_mfma(const u32x4 (&w)[2], uint32_t sv, const u32x4 (&act)[8],
+                                                 bool valid, f32x4 (&acc)[2]) {
+  f16x2 s16{};
+  float smx[2] = {0.f, 0.f};
+  if (FMT == 0) {
+    const _Float16 sh = (_Float16)(valid ? __uint_as_float(sv) * kNf4ScaleUp : 0.0f);
+    s16 = f16x2{sh, sh};
+  } else {
+    smx[0] = valid ? e8m0_to_f32(sv & 0xFFu) : 0.0f;
+    smx[1] = valid ? e8m0_to_f32((sv >> 8) & 0xFFu) : 0.0f;
+  }
+#pragma unroll
+  for (int iq = 0; iq < 8; ++iq) {
+    const int i = iq >> 2, q = iq & 3;
+    uint32_t d[4];
+    u32x4 xv = act[iq];
+    if (FMT == 0) {
+      nf4_decode8(w[i][q], d);
+#pragma unroll
+      for (int bt = 0; bt < 4; ++bt) d[bt] = pk_mul_f16(d[bt], s16);
+      // natural pairs (0,1) (2,3) (4,5) (6,7) -> slot order (0,2) (4,6) (1,3) (5,7)
+      xv = u32x4{perm(xv[1], xv[0], 0x05040100u), perm(xv[3], xv[2], 0x05040100u),
+                 perm(xv[1], xv[0], 0x07060302u), perm(xv[3], xv[2], 0x07060302u)};
+    } else {
+      mxfp4_decode8(w[i][q], smx[i], d);
+    }
+    const f16x8 a = __builtin_bit_cast(f16x8, u32x4{d[0], d[1], d[2], d[3]});
+    acc[iq & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(f16x8, xv), acc[iq & 1], 0, 0, 0);
+  }
+}
+
+// Weight registers of one down-phase unit.
+struct DnUnit {
+  u32x4 w[2];
+  uint32_t sv;
+};
+
+template <int FMT, int PL>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+    moe_decode_step_kernel(DecodeStepArgs p) {
+  __shared__ int32_t s_ids[kDecMaxS];
+  __shared__ float s_w[kDecMaxS];
+  __shared__ int32_t s_sorted[kDecMaxS];     // sorted row -> slot
+  __shared__ int32_t s_tile[3][kDecMaxS];    // expert, first sorted row, rows
+  __shared__ int32_t s_ntiles;
+  __shared__ int32_t s_last;
+  __shared__ __attribute__((aligned(16))) f32x4 part[kThreads];
+  __shared__ float red[kWaves][4][kDecMaxT][4];
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];  // x as fp16, T rows of 2H + 16 bytes
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int T = p.T, k = p.k, S = T * k, E = p.E;
+  const int G = int(gridDim.x);
+  const int r = lane & 15, g = lane >> 4;
+  const uint32_t xrow = uint32_t(2 * p.H + 16);  // LDS row pitch of x (16 bytes of padding)
+
+  // ---- x -> LDS as fp16, natural order
+  // x chunks are spread over the waves that do not route (T < 8), which load them while the
+  // routing waves work; with 8 tokens every wave loads its share after the routing
+  const int nchunk = T * (p.H / 8);
+  const int xw0 = T < kWaves ? T : 0;                    // first loading wave
+  const int xthreads = (kWaves - xw0) * 64;
+  const int xt = tid - xw0 * 64;                         // index among the loading threads
+  const __amdgpu_buffer_rsrc_t xres = rsrc(p.x, uint32_t(int64_t(T) * p.H * 2));
+  auto x_to_lds = [&]() {
+    for (int c = xt; c < nchunk; c += xthreads) {
+      const int t = c / (p.H / 8), k8 = c - t * (p.H / 8);
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xres, uint32_t(c) * 16, 0, 0));
+      *reinterpret_cast<u32x4*>(xs + uint32_t(t) * xrow + 16 * k8) = bf16x8_to_f16x8(v);
+    }
+  };
+  if (T < kWaves && wave >= T) x_to_lds();
+
+  // ---- routing, in every workgroup
+  if (wave < T) {
+    int id;
+    float wt;
+    topk_token<PL>(p.logits + int64_t(wave) * E, E, k, p.renorm, lane, id, wt);
+    if (lane < k) {
+      s_ids[wave * k + lane] = id;
+      s_w[wave * k + lane] = wt;
+      if (blockIdx.x == 0 && p.ids_out) {
+        p.ids_out[wave * k + lane] = id;
+        p.w_out[wave * k + lane] = wt;
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0 && lane < S) {  // rank of slot `lane`: expert-major, then slot (= token) order
+    const int e = s_ids[lane];
+    int rank = 0;
+    for (int q = 0; q < S; ++q) {
+      const int eq = s_ids[q];
+      rank += (eq < e) || (eq == e && q < lane);
+    }
+    s_sorted[rank] = lane;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const bool v = lane < S;
+    const int e = v ? s_ids[s_sorted[lane]] : -1;
+    const bool first = v && (lane == 0 || s_ids[s_sorted[lane - 1]] != e);
+    const uint64_t m = __ballot(first);
+    if (first) {
+      const int ti = __popcll(m & ((uint64_t(1) << lane) - 1));
+      const uint64_t after = lane == 63 ? 0 : (m >> (lane + 1));
+      const int next = after ? lane + 1 + int(__builtin_ctzll(after)) : S;
+      s_tile[0][ti] = e;
+      s_tile[1][ti] = lane;
+      s_tile[2][ti] = next - lane;
+    }
+    if (lane == 0) s_ntiles = __popcll(m);
+    if (blockIdx.x == 0 && v && p.slots_out) p.slots_out[lane] = s_sorted[lane];
+  }
+  if (blockIdx.x == 0 && p.offsets_out) {
+    for (int e = tid; e <= E; e += kThreads) {
+      int c = 0;
+      for (int q = 0; q < S; ++q) c += s_ids[q] < e;
+      p.offsets_out[e] = c;
+    }
+  }
+  if (T >= kWaves) x_to_lds();
+  __syncthreads();
+  const int ntiles = s_ntiles;
+
+  // ---- gate_up + activation -> h (device-coherent stores).  An item (tile, 8 gate + 8 up
+  // rows) is taken by W waves that split its K steps (W = 8, 4, 2 or 1: the largest that still
+  // gives every item its waves in one pass over the grid, so few items get split and many do
+  // not); a wave runs its K steps of its items as one sequence with the next step's weights in
+  // flight (two register sets); the activations come from x in LDS.  With W > 1 an item's last
+  // step adds its waves' sums in LDS.
+  {
+    const int njb = (p.I + 7) / 8;
+    const int items = ntiles * njb;
+    const int nseg = (p.H + kStepK - 1) / kStepK;
+    int W = kWaves;
+    while (W > 1 && int64_t(items) * W > int64_t(G) * kWaves) W >>= 1;
+    const int ipp = kWaves / W;              // items per workgroup pass
+    const int slot = wave / W, kp = wave - slot * W;
+    const int spw = (nseg + W - 1) / W;      // K steps per wave per item
+    const int64_t N = 2 * int64_t(p.I);
+    const uint32_t kb = uint32_t(p.H >> 1);
+    const uint32_t nbs = FMT == 0 ? uint32_t(p.H >> 6) * 4 : uint32_t(p.H >> 5);
+    const __amdgpu_buffer_rsrc_t hres = rsrc(p.h, uint32_t(int64_t(S) * p.I * 2));
+    struct GuLoad {
+      u32x4 w[2];
+      uint32_t sv;
+    };
+    // weights of K step st of item it (clamped item past the end; steps past K read zeros or
+    // the next row, and their scale is 0)
+    auto issue = [&](int it, int st, GuLoad& L) {
+      const int itc = it < items ? it : items - 1;
+      const int a = itc / njb, jb = itc - a * njb;
+      const int e = s_tile[0][a];
+      int32_t j = jb * 8 + (r & 7);
+      j = j < p.I ? j : p.I - 1;
+      const uint32_t row = uint32_t(p.interleaved ? (r < 8 ? 2 * j : 2 * j + 1) : (r < 8 ? j : p.I + j));
+      const __amdgpu_buffer_rsrc_t wres = rsrc(p.w_gu + int64_t(e) * N * kb, uint32_t(N) * kb);
+      const __amdgpu_buffer_rsrc_t sres =
+          rsrc(reinterpret_cast<const uint8_t*>(p.s_gu) + int64_t(e) * N * nbs, uint32_t(N) * nbs);
+      const uint32_t wo = row * kb + 32 * g;
+      const uint32_t so = row * nbs + (FMT == 0 ? 4 * g : 2 * g);
+      const int kstep = (kp + W * st) * kStepK;
+      L.w[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, wo, kstep >> 1, 0));
+      L.w[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, wo + 16, kstep >> 1, 0));
+      L.sv = FMT == 0 ? __builtin_amdgcn_raw_buffer_load_b32(sres, so, (kstep >> 6) * 4, 0)
+                      : uint32_t(__builtin_amdgcn_raw_buffer_load_b16(sres, so, kstep >> 5, 0));
+    };
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // h of item it from the full sums `sum` (held by one wave)
+    auto epilogue = [&](int it, f32x4 sum) {
+      const int a = it / njb, jb = it - a * njb;
+      const int e = s_tile[0][a], row0 = s_tile[1][a], rows = s_tile[2][a];
+      if (FMT == 0) sum *= kNf4ScaleDown;
+      // rows 0-7 of the block are gate rows, 8-15 the matching up rows: lane groups 0/1
+      // hold gate values of (j0 + i, token column r), 2/3 the up values
+      float up[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) up[i] = __shfl_xor(sum[i], 32);
+      if (g < 2 && r < rows) {
+        const int32_t j0 = jb * 8 + 4 * g;
+        uint32_t hv[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int32_t jj = j0 + i;
+          float gv = sum[i], uv = up[i];
+          if (p.b_gu) {
+            gv += p.b_gu[int64_t(e) * N + (p.interleaved ? 2 * jj : jj)];
+            uv += p.b_gu[int64_t(e) * N + (p.interleaved ? 2 * jj + 1 : p.I + jj)];
+          }
+          const _Float16 hh = (_Float16)(p.clamped_glu ? clamped_glu(gv, uv) : swiglu(gv, uv));
+          hv[i >> 1] |= uint32_t(__builtin_bit_cast(uint16_t, hh)) << (16 * (i & 1));
+        }
+        // I % 64 == 0: the 4 columns j0..j0+3 are in range and 8-byte aligned
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{hv[0], hv[1]}, hres,
+                                              uint32_t(row0 + r) * uint32_t(p.I * 2) + 2 * j0, 0, kCohere);
+      }
+    };
+    auto consume = [&](int it, int st, GuLoad& L) {
+      const int kstep = (kp + W * st) * kStepK;
+      if (it < items) {
+        const int a = it / njb;
+        const int row0 = s_tile[1][a], rows = s_tile[2][a];
+        const int c = r < rows ? r : rows - 1;
+        const int t = s_sorted[row0 + c] / k;
+        const uint8_t* xr = xs + uint32_t(t) * xrow + 2 * uint32_t(kstep + 64 * g);
+        u32x4 xa[8];
+        const bool inK = kstep + 64 * g < p.H;  // past K: the scale is 0; read row 0 in range
+#pragma unroll
+        for (int iq = 0; iq < 8; ++iq)
+          xa[iq] = inK ? *reinterpret_cast<const u32x4*>(xr + 16 * iq) : u32x4{0u, 0u, 0u, 0u};
+        decode_step_mfma<FMT>(L.w, L.sv, xa, inK, acc);
+      }
+      if (st != spw - 1) return;
+      if (W == 1) {
+        if (it < items) epilogue(it, acc[0] + acc[1]);
+      } else {
+        part[tid] = acc[0] + acc[1];
+        __syncthreads();
+        if (kp == 0 && it < items) {
+          f32x4 sum = part[tid];
+          for (int w = 1; w < W; ++w) sum += part[tid + 64 * w];
+          epilogue(it, sum);
+        }
+        __syncthreads();
+      }
+      acc[0] = acc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    // step sequence of this wave: items it = blockIdx.x * ipp + slot + m * G * ipp, each with
+    // steps st = 0 .. spw-1; the loop runs over whole passes so every wave of the workgroup
+    // reaches the same LDS barriers
+    const int npass = (items - int(blockIdx.x) * ipp + G * ipp - 1) / (G * ipp);
+    const int nsteps = npass > 0 ? npass * spw : 0;
+    auto item_of = [&](int q) { return int(blockIdx.x) * ipp + slot + (q / spw) * G * ipp; };
+    // ring of 4 register sets: the loads of steps q + 1 .. q + 3 are in flight while step q
+    // is computed
+    GuLoad R0, R1, R2, R3;
+    auto issue_q = [&](int q, GuLoad& L) {
+      if (q < nsteps) issue(item_of(q), q % spw, L);
+    };
+    issue_q(0, R0);
+    issue_q(1, R1);
+    issue_q(2, R2);
+    for (int q = 0; q < nsteps; q += 4) {
+      issue_q(q + 3, R3);
+      consume(item_of(q), q % spw, R0);
+      if (q + 1 >= nsteps) break;
+      issue_q(q + 4, R0);
+      consume(item_of(q + 1), (q + 1) % spw, R1);
+      if (q + 2 >= nsteps) break;
+      issue_q(q + 5, R1);
+      consume(item_of(q + 2), (q + 2) % spw, R2);
+      if (q + 3 >= nsteps) break;
+      issue_q(q + 6, R2);
+      consume(item_of(q + 3), (q + 3) % spw, R3);
+    }
+  }
+
+  // ---- down phase layout (the same in every workgroup): column blocks of 16 outputs, the
+  // tiles cut into ntg groups so that there are about as many items as workgroups
+  const int nseg2 = (p.I + kStepK - 1) / kStepK;
+  const int nblk = (p.H + 15) / 16;
+  int tpg = (ntiles * nblk + G - 1) / G;  // tiles per group
+  tpg = tpg < 1 ? 1 : tpg;
+  int ntg = (ntiles + tpg - 1) / tpg;
+  if (ntg > kDecMaxTG) {
+    ntg = kDecMaxTG;
+    tpg = (ntiles + ntg - 1) / ntg;
+  }
+  const int items2 = nblk * ntg;
+  const uint32_t kb2 = uint32_t(p.I >> 1);
+  const uint32_t nbs2 = FMT == 0 ? uint32_t(p.I >> 6) * 4 : uint32_t(p.I >> 5);
+  // unit u of item (cb, grp): tile grp * tpg + u / nseg2, K step u % nseg2
+  auto unit_count = [&](int grp) {
+    const int t0 = grp * tpg;
+    const int nt = ntiles - t0 < tpg ? ntiles - t0 : tpg;
+    return nt * nseg2;
+  };
+  auto load_unit = [&](int cb, int grp, int u, DnUnit& U) {
+    const int a = grp * tpg + u / nseg2, seg = u % nseg2;
+    const int e = s_tile[0][a];
+    const int n0 = cb * 16;
+    const uint32_t row = uint32_t(n0 + r < p.H ? n0 + r : p.H - 1);
+    const __amdgpu_buffer_rsrc_t wres = rsrc(p.w_dn + int64_t(e) * p.H * kb2, uint32_t(p.H) * kb2);
+    const __amdgpu_buffer_rsrc_t sres =
+        rsrc(reinterpret_cast<const uint8_t*>(p.s_dn) + int64_t(e) * p.H * nbs2, uint32_t(p.H) * nbs2);
+    const uint32_t wo = row * kb2 + 32 * g;
+    const uint32_t so = row * nbs2 + (FMT == 0 ? 4 * g : 2 * g);
+    const int kstep = seg * kStepK;
+    U.w[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, wo, kstep >> 1, 0));
+    U.w[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, wo + 16, kstep >> 1, 0));
+    U.sv = FMT == 0 ? __builtin_amdgcn_raw_buffer_load_b32(sres, so, (kstep >> 6) * 4, 0)
+                    : uint32_t(__builtin_amdgcn_raw_buffer_load_b16(sres, so, kstep >> 5, 0));
+  };
+
+  // ---- grid barrier.  h is stored device-coherently; its stores are complete (vmcnt 0) in
+  // every wave before the workgroup arrives.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+  __builtin_amdgcn_s_barrier();
+  const int q = int(blockIdx.x) % kDecGroups;
+  const int ngrp = G < kDecGroups ? G : kDecGroups;
+  if (tid == 0) {
+    const uint32_t gsize = uint32_t((G - 1 - q) / kDecGroups + 1);  // workgroups with this residue
+    const uint32_t o = __hip_atomic_fetch_add(&p.ctl[kCtlGrp + 16 * q], 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    if (o == gsize - 1) {
+      const uint32_t o2 = __hip_atomic_fetch_add(&p.ctl[kCtlTop], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (o2 == uint32_t(ngrp) - 1)
+        for (int qq = 0; qq < ngrp; ++qq)
+          __hip_atomic_store(&p.ctl[kCtlGo + 16 * qq], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  // the first down unit's weights do not depend on h: load them while the barrier is pending
+  DnUnit pre;
+  const int it0 = int(blockIdx.x);
+  const bool have_pre = it0 < items2 && wave < unit_count(it0 % ntg);
+  if (have_pre) load_unit(it0 / ntg, it0 % ntg, wave, pre);
+  if (tid == 0) {
+    int spins = 0;
+    while (__hip_atomic_load(&p.ctl[kCtlGo + 16 * q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+      if (spins >= p.spin_limit) {
+        __hip_atomic_fetch_or(&p.ctl[kCtlGaveUp], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      ++spins;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __builtin_amdgcn_s_barrier();
+
+  // ---- down + weighted combine -> column-block sums -> out
+  {
+    const __amdgpu_buffer_rsrc_t hres = rsrc(p.h, uint32_t(int64_t(S) * p.I * 2));
+    const __amdgpu_buffer_rsrc_t pres = rsrc(p.part, uint32_t(nblk) * kDecMaxTG * kDecMaxT * 16 * 4);
+    for (int it = int(blockIdx.x); it < items2; it += G) {
+      const int cb = it / ntg, grp = it - cb * ntg;
+      const int n0 = cb * 16;
+      const int nu = unit_count(grp);
+      float acc_t[kDecMaxT][4];
+#pragma unroll
+      for (int t = 0; t < kDecMaxT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc_t[t][i] = 0.f;
+      for (int u = wave; u < nu; u += kWaves) {
+        DnUnit U;
+        if (it == it0 && u == wave) {
+          U = pre;
+        } else {
+          load_unit(cb, grp, u, U);
+        }
+        const int a = grp * tpg + u / nseg2, seg = u % nseg2;
+        const int e = s_tile[0][a], row0 = s_tile[1][a], rows = s_tile[2][a];
+        const int c = r < rows ? r : rows - 1;
+        const int kstep = seg * kStepK;
+        const uint32_t ao = uint32_t(row0 + c) * uint32_t(p.I * 2) + 128 * g;
+        u32x4 ha[8];
+#pragma unroll
+        for (int iq = 0; iq < 8; ++iq)
+          ha[iq] = __builtin_bit_cast(u32x4,
+                                      __builtin_amdgcn_raw_buffer_load_b128(hres, ao + 16 * iq, 2 * kstep, kCohere));
+        f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        decode_step_mfma<FMT>(U.w, U.sv, ha, int64_t(64 * g) < int64_t(p.I) - kstep, acc);
+        f32x4 d = acc[0] + acc[1];
+        if (FMT == 0) d *= kNf4ScaleDown;
+        if (seg == 0 && p.b_dn) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int n = n0 + 4 * g + i;
+            d[i] += n < p.H ? p.b_dn[int64_t(e) * p.H + n] : 0.0f;
+          }
+        }
+        if (r < rows) {
+          const int slot = s_sorted[row0 + r];
+          const int t = slot / k;
+          const float wt = s_w[slot];
+#pragma unroll
+          for (int tt = 0; tt < kDecMaxT; ++tt)
+            if (tt == t) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc_t[tt][i] += wt * d[i];
+            }
+        }
+      }
+      // per token: the 16 lanes of a row group hold different slots; add them (fixed order)
+#pragma unroll
+      for (int tt = 0; tt < kDecMaxT; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = acc_t[tt][i];
+          v += __shfl_xor(v, 1);
+          v += __shfl_xor(v, 2);
+          v += __shfl_xor(v, 4);
+          v += __shfl_xor(v, 8);
+          if (r == 0 && tt < T) red[wave][g][tt][i] = v;
+        }
+      __syncthreads();
+      // this item's sums over its tiles -> part[cb][grp] (device-coherent stores)
+      if (tid < T * 16) {
+        const int t = tid >> 4, rr = tid & 15;
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) sum += red[w][rr >> 2][t][rr & 3];
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), pres,
+                                              uint32_t(((cb * kDecMaxTG + grp) * kDecMaxT + t) * 16 + rr) * 4, 0,
+                                              kCohere);
+      }
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
+      __syncthreads();
+      if (tid == 0) {
+        const uint32_t o = __hip_atomic_fetch_add(&p.ctl[kCtlCols + cb], 1u, __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT);
+        s_last = o == uint32_t(ntg) - 1;
+        if (s_last) __hip_atomic_store(&p.ctl[kCtlCols + cb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+      if (s_last && tid < T * 16) {  // every group of these columns is stored: add them in order
+        const int t = tid >> 4, rr = tid & 15;
+        float sum = 0.f;
+        for (int gg = 0; gg < ntg; ++gg)
+          sum += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              pres, uint32_t(((cb * kDecMaxTG + gg) * kDecMaxT + t) * 16 + rr) * 4, 0, kCohere));
+        const int n = n0 + rr;
+        if (n < p.H) {
+          if (p.out_f32) p.out_f32[int64_t(t) * p.H + n] = sum;
+          p.out[int64_t(t) * p.H + n] = f32_to_bf16_rne(sum);
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- exit: the last workgroup resets the barrier words for the next call
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t d = __hip_atomic_fetch_add(&p.ctl[kCtlDepart], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == uint32_t(G) - 1) {
+      const uint32_t gave_up = __hip_atomic_load(&p.ctl[kCtlGaveUp], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (p.status) *p.status = gave_up ? 1 : 0;
+      for (int qq = 0; qq < kDecGroups; ++qq) {
+        __hip_atomic_store(&p.ctl[kCtlGrp + 16 * qq], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.ctl[kCtlGo + 16 * qq], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __hip_atomic_store(&p.ctl[kCtlTop], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&p.ctl[kCtlGaveUp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&p.ctl[kCtlDepart], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 int cu_count() {
   static std::atomic<int> cached[64];  // 0 = not read yet; the value read is idempotent
   int dev = 0;
@@ -638,6 +1169,79 @@ static hipError_t launch_gemv_fmt(const MoeLaunch& L, const TileList& tl, hipStr
   g.K = L.I;
   g.N = L.H;
   return launch_stage<FMT, false, SLOT>(g, tl, L, L.y, L.H, stream);
+}
+
+// Single-launch decode step: a grid of co-resident workgroups (at most what the device holds at
+// once, so the grid barrier cannot wait on a workgroup that is not running).
+template <int FMT, int PL>
+static hipError_t launch_decode_pl(const DecodeStepArgs& a, int64_t items, hipStream_t stream) {
+  // x in LDS: T rows of 2H + 16 bytes (at most 64 KB + padding); the occupancy is taken at the
+  // largest size, once per device, with the dynamic-LDS limit raised for it
+  constexpr size_t kMaxXs = size_t(kDecXChunks) * kThreads * 16 + kDecMaxT * 16;
+  const size_t lds = size_t(a.T) * size_t(2 * a.H + 16);
+  static std::atomic<int> occ_cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  int occ = occ_cache[dev].load(std::memory_order_relaxed);
+  if (occ == 0) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(moe_decode_step_kernel<FMT, PL>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxXs)) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, moe_decode_step_kernel<FMT, PL>, kThreads, kMaxXs) !=
+            hipSuccess || occ <= 0)
+      return hipErrorInvalidValue;
+    occ_cache[dev].store(occ, std::memory_order_relaxed);
+  }
+  int64_t grid = int64_t(occ < 2 ? occ : 2) * cu_count();
+  if (grid > items) grid = items;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL((moe_decode_step_kernel<FMT, PL>), dim3(unsigned(grid)), dim3(kThreads), lds, stream, a);
+  return hipGetLastError();
+}
+
+size_t decode_ctl_bytes(int64_t H) {
+  const size_t words = size_t(kCtlCols) + size_t((H + 15) / 16);
+  return (words * 4 + 255) / 256 * 256;
+}
+
+hipError_t launch_decode_step(const DecodeLaunch& L, hipStream_t stream) {
+  DecodeStepArgs a{};
+  a.E = int32_t(L.E);
+  a.H = int32_t(L.H);
+  a.I = int32_t(L.I);
+  a.T = int32_t(L.T);
+  a.k = L.k;
+  a.renorm = L.renorm;
+  a.clamped_glu = L.clamped_glu;
+  a.interleaved = L.interleaved;
+  a.spin_limit = L.spin_limit;
+  a.logits = L.logits;
+  a.x = L.x;
+  a.w_gu = L.w_gu;
+  a.s_gu = L.s_gu;
+  a.w_dn = L.w_dn;
+  a.s_dn = L.s_dn;
+  a.b_gu = L.b_gu;
+  a.b_dn = L.b_dn;
+  a.ids_out = L.ids;
+  a.w_out = L.w;
+  a.offsets_out = L.offsets;
+  a.slots_out = L.slots;
+  a.out = L.out;
+  a.out_f32 = L.out_f32;
+  a.h = L.h;
+  a.part = L.part;
+  a.ctl = L.ctl;
+  a.status = L.status;
+  const int64_t S = L.T * L.k;
+  const int64_t active = L.E < S ? L.E : S;
+  const int64_t items1 = active * ((L.I + 7) / 8), items2 = (L.H + 15) / 16;
+  const int64_t items = items1 > items2 ? items1 : items2;
+  const bool nf4 = L.fmt == 0;
+  if (L.E <= 64) return nf4 ? launch_decode_pl<0, 1>(a, items, stream) : launch_decode_pl<1, 1>(a, items, stream);
+  if (L.E <= 128) return nf4 ? launch_decode_pl<0, 2>(a, items, stream) : launch_decode_pl<1, 2>(a, items, stream);
+  if (L.E <= 256) return nf4 ? launch_decode_pl<0, 4>(a, items, stream) : launch_decode_pl<1, 4>(a, items, stream);
+  return nf4 ? launch_decode_pl<0, kMaxExpertsPerLane>(a, items, stream)
+             : launch_decode_pl<1, kMaxExpertsPerLane>(a, items, stream);
 }
 
 hipError_t launch_gemv(const MoeLaunch& L, hipStream_t stream, int stage) {

@@ -225,6 +225,58 @@ int e4b_moe_forward_noalloc(const e4b_moe_args* a, void* stream);
 /* Bytes of the scratch e4b_moe_forward_noalloc uses (a compile-time constant). */
 size_t e4b_noalloc_scratch_bytes(void);
 
+/* Arguments of e4b_moe_decode_step.  Sizes: 1 <= T <= 8, T*k <= 64, T*H <= 32768, E <= 1024,
+ * H % 64 == 0, I % 64 == 0, I*H < 2^31. */
+typedef struct e4b_decode_args {
+  int32_t fmt;            /* e4b_fmt */
+  int32_t k;              /* experts per token */
+  int64_t E, H, I, T;
+  int32_t route_flags;    /* E4B_ROUTE_RENORMALIZE or 0, as for e4b_route_permute */
+  int32_t flags;          /* E4B_ACT_CLAMPED_GLU | E4B_GU_INTERLEAVED, as for e4b_moe_forward */
+  const float* logits;    /* [T, E] float32 router logits */
+  const uint16_t* x;      /* [T, H] bf16 bits; |x| <= 65504 */
+  const uint8_t* w_gu;    /* packed gate_up stack, as for e4b_moe_forward */
+  const void* s_gu;
+  const uint8_t* w_dn;    /* packed down stack */
+  const void* s_dn;
+  const float* b_gu;      /* NULL or [E, 2I] float32 */
+  const float* b_dn;      /* NULL or [E, H] float32 */
+  int32_t* topk_ids;      /* NULL or [T, k] out: as e4b_route_permute */
+  float* topk_w;          /* NULL or [T, k] out (both or neither of topk_ids / topk_w) */
+  int32_t* expert_offsets; /* NULL or [E+1] out */
+  int32_t* sorted_slots;  /* NULL or [T*k] out */
+  uint16_t* out;          /* [T, H] bf16 out: RNE of the fp32 result */
+  float* out_f32;         /* NULL or [T, H] float32 out */
+  int32_t* status;        /* NULL or one int32 out: 0, or 1 if the grid barrier gave up waiting
+                           * (then `out` is not valid) */
+  int32_t spin_limit;     /* polls of the grid barrier before it gives up; 0 = the default
+                           * (about a million polls, under a second); negative = do not
+                           * wait (for tests of the give-up path) */
+  int32_t reserved;       /* must be 0 */
+  void* ws;               /* device workspace of at least e4b_decode_workspace_bytes(), zero-filled
+                           * before the first call with it (e.g. at allocation): its head holds
+                           * the kernel's counters, which every call leaves zero again */
+  size_t ws_bytes;
+} e4b_decode_args;
+
+/* Workspace bytes e4b_moe_decode_step needs for the sizes in `a`. */
+int e4b_decode_workspace_bytes(const e4b_decode_args* a, size_t* bytes);
+
+/*
+ * e4b_moe_decode_step — one decode step for a few tokens in a single launch: the router
+ * epilogue of e4b_route_permute (bit-identical ids, weights, offsets and slots), the grouped
+ * gate_up products with the activation, the down products and the weighted combine of
+ * e4b_moe_forward (the same fp16-operand / fp32-accumulation numerics, the same tolerance),
+ * fused so that the step costs one kernel launch (grouped-nf4-gemm 0.25.0 project
+ * description, "What is measured", limit 1: at decode the fused path loses to a CUDA-graphed
+ * baseline, its launches costing more than its bytes; the opening section names the router
+ * epilogue among the decode glue kernels).  The kernel's workgroups meet once at a grid
+ * barrier (between the gate_up and the down products); the grid never exceeds what the device
+ * holds at once.  Calls sharing a workspace must not overlap; calls with distinct workspaces
+ * may run concurrently.  The result is deterministic run to run.
+ */
+int e4b_moe_decode_step(const e4b_decode_args* a, void* stream);
+
 /* Arguments of e4b_grouped_dgrad. */
 typedef struct e4b_dgrad_args {
   int32_t fmt;            /* e4b_fmt */

@@ -137,6 +137,39 @@ def test_noalloc_forward_rejects_bad_arguments(e4b):
     assert e4b.e4b_status_string(-8).startswith("the call needs more workspace")
 
 
+def _dargs(e4b, **kw):
+    a = e4b.DecodeArgs()
+    a.fmt, a.k, a.E, a.H, a.I, a.T = 0, 8, 128, 2048, 768, 4
+    for f in ("logits", "x", "w_gu", "s_gu", "w_dn", "s_dn", "out", "ws"):
+        setattr(a, f, FAKE)
+    a.ws_bytes = 1 << 40
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_decode_step_rejects_bad_arguments(e4b):
+    f = lambda **kw: e4b._c_decode_step(ctypes.byref(_dargs(e4b, **kw)), None)
+    assert f(T=9) == ERR_SHAPE
+    assert f(T=0) == ERR_SHAPE
+    assert f(T=8, k=9) == ERR_SHAPE            # 72 routed slots
+    assert f(E=1025, k=8) == ERR_SHAPE
+    assert f(k=0) == ERR_ARG
+    assert f(fmt=2) == ERR_ARG
+    assert f(route_flags=2) == ERR_ARG
+    assert f(flags=1) == ERR_ARG               # a path flag is not a decode-step flag
+    assert f(reserved=1) == ERR_ARG
+    assert f(H=96) == ERR_SHAPE
+    assert f(x=None) == ERR_ARG
+    assert f(ws=None) == ERR_ARG
+    assert f(topk_ids=FAKE) == ERR_ARG         # ids without weights
+    assert f(out=FAKE + 2) == ERR_ALIGN
+    assert f(ws_bytes=1024) == ERR_WORKSPACE
+    n = ctypes.c_size_t(0)
+    assert e4b._c_decode_ws(ctypes.byref(_dargs(e4b)), ctypes.byref(n)) == 0
+    assert n.value >= 256 + 4 * 8 * 768 * 2
+
+
 def test_workspace_sizes_cover_the_intermediates(e4b):
     from moe_inputs import WORKLOADS
     for wl in WORKLOADS.values():
