@@ -89,9 +89,10 @@ class Batch:
     flags = 0
     variant = {}  # expert-variant keyword arguments of e4b_moe_forward (act, interleaved, biases)
 
-    def __init__(self, layer: Layer, T: int):
+    def __init__(self, layer: Layer, T: int, flags: int = 0):
         torch, e4b = layer.torch, layer.e4b
         self.layer, self.e4b = layer, e4b
+        self.flags = flags
         self.wl = wl = layer.wl.with_T(T)
         dev = "cuda:0"
         self.x = torch.from_numpy(make_x(wl).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -102,7 +103,7 @@ class Batch:
                           torch.empty((T * wl.k,), dtype=torch.int32, device=dev))
         self.route_ws = torch.empty(max(256, e4b.e4b_route_workspace_bytes(T, wl.E, wl.k)),
                                     dtype=torch.uint8, device=dev)
-        self.fwd_ws = torch.empty(max(256, e4b.e4b_moe_workspace_bytes(wl.fmt, wl.E, wl.H, wl.I, T, wl.k)),
+        self.fwd_ws = torch.empty(max(256, e4b.e4b_moe_workspace_bytes(wl.fmt, wl.E, wl.H, wl.I, T, wl.k, flags)),
                                   dtype=torch.uint8, device=dev)
         self.out = torch.empty((T, wl.H), dtype=torch.bfloat16, device=dev)
 
@@ -309,8 +310,7 @@ def blas_threads() -> str:
 
 def batch_report(torch, layer: Layer, T: int, steps: int, warmup: int, flush: int = 0, flags: int = 0,
                  graph: bool = False, variant: dict | None = None):
-    b = Batch(layer, T)
-    b.flags = flags
+    b = Batch(layer, T, flags)
     b.variant = variant or {}
     wl = b.wl
     n_active = b.active_experts()

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libe4b.so")
-SOURCES = ["abi.hip", "pack.hip", "route.hip", "moe.hip", "gemv.hip", "dgrad.hip", "int4.hip", "probe.hip"]
+SOURCES = ["abi.hip", "pack.hip", "route.hip", "moe.hip", "gemv.hip", "dgrad.hip", "int4.hip", "probe.hip", "scaled.hip"]
 
 
 def hipcc() -> str:

@@ -11,6 +11,8 @@
 namespace {
 
 constexpr size_t kAlign = 256;
+// MXFP4 gate_up on the block-scaled instruction unless E4B_MXFP4_FP16 is given
+constexpr bool kScaledByDefault = false;
 constexpr int kMaxDevices = 64;
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -88,15 +90,32 @@ Tile pick_tile(const e4b_moe_args* a) {
 }
 
 struct FwdLayout {
-  int bm, waves, gemv;
+  int bm, waves, gemv, scaled;
   int64_t max_mtiles, max_stiles;
   int tail_rows;
-  size_t off_x16, off_h, off_y, off_inv, off_tok, off_tiles, off_n, total;
+  size_t off_x16, off_h, off_y, off_inv, off_tok, off_tiles, off_n, off_x8, off_xsc, total;
 };
+
+// Route of an MXFP4 gate_up on MFMA tiles: the block-scaled fp8 x fp4 instruction or fp16
+// operands decoded in registers.
+bool use_scaled(const e4b_moe_args* a, const Tile& t) {
+  if (a->fmt != E4B_FMT_MXFP4 || t.gemv || t.bm < 128) return false;
+  const int r = a->flags & E4B_MXFP4_ROUTE_MASK;
+  if (r == E4B_MXFP4_SCALED) return true;
+  if (r == E4B_MXFP4_FP16) return false;
+  return kScaledByDefault;
+}
+
+// The tile, with the scaled route's 128-row tiles where it applies.
+Tile pick_route_tile(const e4b_moe_args* a) {
+  Tile t = pick_tile(a);
+  if (use_scaled(a, t)) t = Tile{128, 4, 0};
+  return t;
+}
 
 int layout_forward(const e4b_moe_args* a, FwdLayout* L) {
   const int64_t S = a->T * a->k;
-  const Tile t = pick_tile(a);
+  const Tile t = pick_route_tile(a);
   L->bm = t.bm;
   L->waves = t.waves;
   L->gemv = t.gemv;
@@ -121,6 +140,14 @@ int layout_forward(const e4b_moe_args* a, FwdLayout* L) {
   off += align_up(size_t(L->max_mtiles + L->max_stiles) * 16);
   L->off_n = off;
   off += kAlign;
+  L->scaled = use_scaled(a, t) ? 1 : 0;
+  L->off_x8 = off;
+  L->off_xsc = off;
+  if (L->scaled) {
+    off += align_up(size_t(a->T) * size_t(a->H) * 2);
+    L->off_xsc = off;
+    off += align_up(size_t(a->T) * size_t(e4b::scale_pitch(a->H)));
+  }
   L->total = off;
   return E4B_OK;
 }
@@ -130,7 +157,9 @@ int check_forward_shape(const e4b_moe_args* a) {
   if (a->fmt != E4B_FMT_NF4 && a->fmt != E4B_FMT_MXFP4) return E4B_ERR_ARG;
   if (a->E <= 0 || a->H <= 0 || a->I <= 0 || a->T < 0 || a->k < 1) return E4B_ERR_ARG;
   if (a->k > a->E) return E4B_ERR_ARG;
-  if ((a->flags & ~(E4B_PATH_MASK | E4B_TILE_MASK | E4B_ACT_CLAMPED_GLU | E4B_GU_INTERLEAVED)) != 0 ||
+  if ((a->flags & ~(E4B_PATH_MASK | E4B_TILE_MASK | E4B_ACT_CLAMPED_GLU | E4B_GU_INTERLEAVED |
+                    E4B_MXFP4_ROUTE_MASK)) != 0 ||
+      (a->flags & E4B_MXFP4_ROUTE_MASK) == E4B_MXFP4_ROUTE_MASK ||
       (a->flags & E4B_PATH_MASK) == 3)
     return E4B_ERR_ARG;
   // a row-tile override names an MFMA tile; it cannot go with the streaming path
@@ -430,6 +459,9 @@ int forward_impl(const e4b_moe_args* a, char* ws, hipStream_t stream) {
   M.tok = reinterpret_cast<int32_t*>(ws + L.off_tok);
   M.tiles = reinterpret_cast<int32_t*>(ws + L.off_tiles);
   M.n_mtiles = reinterpret_cast<int32_t*>(ws + L.off_n);
+  M.scaled = L.scaled;
+  M.x8 = reinterpret_cast<uint8_t*>(ws + L.off_x8);
+  M.xsc = reinterpret_cast<uint8_t*>(ws + L.off_xsc);
   M.events = a->stage_events;
   return launched(e4b::launch_moe_forward(M, stream));
 }

@@ -52,6 +52,7 @@ struct MoeLaunch {
   const float* b_dn;  // nullable [E, H]
   int clamped_glu;    // activation: 0 silu(G) * U, 1 clamped GLU
   int interleaved;    // gate_up rows: 0 halves, 1 interleaved
+  int scaled;         // MXFP4 gate_up on the block-scaled fp8 x fp4 instruction (MFMA tiles)
   // workspace carve-outs
   _Float16* x16;   // [T, H]
   _Float16* h;     // [S, I]
@@ -60,10 +61,16 @@ struct MoeLaunch {
   int32_t* tok;    // [S]: sorted row -> token (slot / k)
   int32_t* tiles;  // [max_mtiles + max_stiles, 4]: main tiles, then tail tiles
   int32_t* n_mtiles;  // [2]: main and tail tile counts
+  uint8_t* x8;        // [T, 2H] activation fp8 parts (scaled route)
+  uint8_t* xsc;       // [T, scale_pitch(H)] activation e8m0 scales (scaled route)
   void* const* events;  // nullable: 6 hipEvent_t around the 5 stages
 };
 
 hipError_t launch_moe_forward(const MoeLaunch& L, hipStream_t stream);
+// MXFP4 gate_up on the block-scaled instruction (128-row MFMA tiles, then tails); its activation
+// scale rows hold scale_pitch(K) bytes.
+hipError_t launch_gate_up_scaled(const MoeLaunch& L, hipStream_t stream);
+__host__ __device__ int64_t scale_pitch(int64_t K);
 
 // The tile list of build_tiles as its own launch (bm-row tiles, no tail tiles).
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, int32_t* tiles,

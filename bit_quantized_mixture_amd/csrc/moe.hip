@@ -670,7 +670,8 @@ static hipError_t launch_gemms(const MoeLaunch& L, hipStream_t stream) {
   g.bias = L.b_gu;
   g.K = L.H;
   g.N = 2 * L.I;
-  hipError_t err = launch_stage_tiles<FMT, true, BM, WAVES>(L, g, stream);
+  hipError_t err = (FMT == 1 && L.scaled && BM >= 128) ? launch_gate_up_scaled(L, stream)
+                                                       : launch_stage_tiles<FMT, true, BM, WAVES>(L, g, stream);
   if (err != hipSuccess) return err;
   record(L, 3, stream);
   // down + routing weight

@@ -108,6 +108,16 @@ typedef enum e4b_fmt { E4B_FMT_NF4 = 0, E4B_FMT_MXFP4 = 1 } e4b_fmt;
  *                        (default: rows 0..I-1 gate, I..2I-1 up) */
 #define E4B_ACT_CLAMPED_GLU 0x10
 #define E4B_GU_INTERLEAVED 0x20
+/* e4b_moe_args.flags bits 6-7: the route of an MXFP4 gate_up on MFMA tiles (0 = the library's
+ * default).  E4B_MXFP4_SCALED: the block-scaled fp8 x fp4 matrix instruction of gfx950 takes the
+ * released e2m1 bytes and e8m0 scales as they are, and the bf16 activations exactly as two fp8
+ * e4m3 parts under an e8m0 scale per 32 (two instructions per product; remainders below 2^-9 of
+ * a block's largest activation rounded to 2^-10 of it).  E4B_MXFP4_FP16: weights decoded to
+ * fp16 in registers, fp16 matrix instruction.  Both: E4B_ERR_ARG.  Ignored for NF4 and for the
+ * streaming path. */
+#define E4B_MXFP4_SCALED 0x40
+#define E4B_MXFP4_FP16 0x80
+#define E4B_MXFP4_ROUTE_MASK 0xC0
 
 /*
  * e4b_pack_nf4 — quantise bf16 expert stacks to NF4.
