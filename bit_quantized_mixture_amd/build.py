@@ -34,6 +34,37 @@ def compile_cmd(out: str) -> list[str]:
     ]
 
 
+def resource_usage(source: str) -> dict[str, dict[str, int]]:
+    """Register use of every kernel of one source file, as the compiler reports it
+    (-Rpass-analysis=kernel-resource-usage on a device-only compile): mangled kernel name ->
+    {"vgpr", "agpr", "vgpr_spill", "scratch", "occupancy"}."""
+    import re
+    import tempfile
+
+    flags = compile_cmd("x")[1:]
+    flags = [f for f in flags if f not in ("-shared", "-o", "x") and not f.endswith(".hip")]
+    with tempfile.TemporaryDirectory() as tmp:
+        cmd = [hipcc(), *flags, "--cuda-device-only", "-c", os.path.join(CSRC, source),
+               "-o", os.path.join(tmp, "k.o"), "-Rpass-analysis=kernel-resource-usage"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + r.stderr[-4000:])
+    keys = {"VGPRs": "vgpr", "AGPRs": "agpr", "VGPRs Spill": "vgpr_spill",
+            "ScratchSize [bytes/lane]": "scratch", "Occupancy [waves/SIMD]": "occupancy"}
+    out: dict[str, dict[str, int]] = {}
+    cur = None
+    for ln in r.stderr.splitlines():
+        m = re.search(r"remark:\s+(Function Name|[A-Za-z][A-Za-z /\[\]]*?): (\S+)", ln)
+        if not m:
+            continue
+        key, val = m.group(1).strip(), m.group(2)
+        if key == "Function Name":
+            cur = out.setdefault(val, {})
+        elif cur is not None and key in keys:
+            cur[keys[key]] = int(val)
+    return out
+
+
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     cmd = compile_cmd(tmp)

@@ -57,6 +57,7 @@ struct GemmArgs {
   const float* bias;       // nullable [E, N]: added to the products (GU before the activation)
   int32_t clamped_glu;     // GU activation: 0 silu(G) * U, 1 clamped GLU
   int32_t interleaved;     // GU rows: 0 halves (gate j, up I + j), 1 interleaved (2j, 2j + 1)
+  int32_t xcd_order;       // 1: workgroup ids dealt to the 8 XCDs in contiguous chunks
 };
 
 
@@ -74,8 +75,17 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
-  const int nt = blockIdx.x % p.n_ntiles;
-  const int mt = blockIdx.x / p.n_ntiles;
+  // Workgroups go to the XCDs round robin (id % 8).  With xcd_order, XCD x takes a
+  // contiguous chunk of the real (row tile, column tile) ids, in order, instead.
+  int bid = int(blockIdx.x);
+  if (p.xcd_order) {
+    const int G = *p.n_mtiles * p.n_ntiles;
+    if (bid >= G) return;
+    const int q = G >> 3, r = G & 7, x = bid & 7;
+    bid = x * q + (x < r ? x : r) + (bid >> 3);
+  }
+  const int nt = bid % p.n_ntiles;
+  const int mt = bid / p.n_ntiles;
   if (mt >= *p.n_mtiles) return;
   const int e = p.tiles[4 * mt], row0 = p.tiles[4 * mt + 1], rows = p.tiles[4 * mt + 2];
 
@@ -363,11 +373,19 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
   decode(bg[0], 0, 0, step_scale(0, 0, 0), step_scale(0, 1, 0), bcur);
   // the weight tile's reads are complete before step 0 refills it
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(63));
-  for (int G = 0; G < ng; ++G) {
+  // A last group holding a single 64-wide step keeps its K in half 0's steps 0 and 1 (steps 2
+  // and 3 would only add zero-scaled products): it runs two steps (K = 2880: 46 steps, not 48).
+  const bool short_last = nk - 4 * (ng - 1) == 1;
+  const int nfull = ng - (short_last ? 1 : 0);
+  for (int G = 0; G < nfull; ++G) {
     kstep(G, std::integral_constant<int, 0>{});
     kstep(G, std::integral_constant<int, 1>{});
     kstep(G, std::integral_constant<int, 2>{});
     kstep(G, std::integral_constant<int, 3>{});
+  }
+  if (short_last) {
+    kstep(nfull, std::integral_constant<int, 0>{});
+    kstep(nfull, std::integral_constant<int, 1>{});
   }
   // drain the DMA issued past the last step before the workgroup's LDS is released
   __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
@@ -646,7 +664,13 @@ static hipError_t launch_stage_tiles(const MoeLaunch& L, GemmArgs g, hipStream_t
   const int per_wave = GU ? 32 : 64;
   g.tiles = L.tiles;
   g.n_mtiles = L.n_mtiles;
+
   g.n_ntiles = int((n_out + WAVES * per_wave - 1) / (WAVES * per_wave));
+  // XCD-local order when a row tile's column sweep fits one XCD's 32 CUs (one round): its
+  // workgroups then share the activation tile in that XCD's L2.  Measured on one box: the
+  // skewed 64-expert layer 6.12 -> 6.03 ms/step, the MXFP4 layer 0.679 -> 0.665 ms; with 112
+  // column tiles (the Mixtral-shaped layer) the same order was 3 % slower.
+  g.xcd_order = g.n_ntiles <= 32;
   hipLaunchKernelGGL((moe_gemm_kernel<FMT, GU, BM, WAVES>),
                      dim3(unsigned(L.max_mtiles * g.n_ntiles)), dim3(WAVES * 64), 0, stream, g);
   if (L.max_stiles > 0) return launch_gemv_tails(L, stream, GU ? 0 : 1);

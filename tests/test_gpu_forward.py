@@ -6,7 +6,7 @@ import pytest
 import torch
 
 from gpu_helpers import (Layer, assert_out_is_rne_of_f32, assert_rows_within_tolerance,
-                         random_layer)
+                         host, random_layer)
 from moe_inputs import WORKLOADS, make_logits, make_weights, make_x
 
 pytestmark = pytest.mark.gpu
@@ -103,7 +103,8 @@ def test_zero_input_gives_zero_output(e4b, tiny):
 @pytest.mark.parametrize("path", [1, 2])
 def test_graph_replay_matches_eager(e4b, path):
     """route + forward captured in a HIP graph: every replay (with eager work and
-    synchronisations in between) reproduces the eager result bit for bit."""
+    synchronisations in between) reproduces the eager result bit for bit, and that result is
+    within the per-row bound of the float64 oracle."""
     layer = random_layer(e4b, "nf4", 16, 256, 256, 24, 4, seed=11)
     T, k, E = layer.T, layer.k, layer.E
     dev = "cuda:0"
@@ -125,6 +126,7 @@ def test_graph_replay_matches_eager(e4b, path):
     step()
     torch.cuda.synchronize()
     ref = out32.clone()
+    assert_rows_within_tolerance(host(ref), layer.oracle_out(), f"graph/{path}")
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
