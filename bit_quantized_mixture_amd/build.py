@@ -65,21 +65,39 @@ def resource_usage(source: str) -> dict[str, dict[str, int]]:
     return out
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = compile_cmd(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
+def build(verbose: bool = False, out: str = LIB) -> str:
+    """Compile every source to an object in parallel (one hipcc per source), then link the
+    shared library; the result replaces `out` only when every step succeeded."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    flags = [f for f in compile_cmd("x")[1:] if f not in ("-shared", "-o", "x") and not f.endswith(".hip")]
     # the host pass does not know the packed-fp32 target feature; that warning is harmless
     noise = "is not a recognized feature for this target"
-    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln and ln.strip()]
-    if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-    if verbose and msgs:
-        print("\n".join(msgs), file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+
+    def run(cmd):
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln and ln.strip()]
+        return r.returncode, msgs
+
+    with tempfile.TemporaryDirectory() as tmp:
+        objs = [os.path.join(tmp, s.replace(".hip", ".o")) for s in SOURCES]
+        cmds = [[hipcc(), *flags, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(min(len(cmds), max(1, os.cpu_count() or 1))) as ex:
+            results = list(ex.map(run, cmds))
+        for rc, msgs in results:
+            if rc != 0:
+                raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+            if verbose and msgs:
+                print("\n".join(msgs), file=sys.stderr)
+        tmp_out = out + ".tmp"
+        rc, msgs = run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp_out])
+        if rc != 0:
+            raise RuntimeError("link failed:\n" + "\n".join(msgs))
+    os.replace(tmp_out, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -18,6 +18,10 @@ struct TileCfg {
 };
 
 constexpr int kGemvTileRows = 16;
+constexpr int kTileCounts = 8;  // ints of tile counts written by the tile-list builder
+
+// Compute units of the current device (cached per device).
+int cu_count();
 
 hipError_t launch_pack_nf4(const uint16_t* w, int64_t n_elems, uint8_t* packed, float* absmax,
                            hipStream_t stream);
@@ -60,7 +64,7 @@ struct MoeLaunch {
   int32_t* inv;    // [S]: slot -> sorted row
   int32_t* tok;    // [S]: sorted row -> token (slot / k)
   int32_t* tiles;  // [max_mtiles + max_stiles, 4]: main tiles, then tail tiles
-  int32_t* n_mtiles;  // [2]: main and tail tile counts
+  int32_t* n_mtiles;  // [kTileCounts]: tile counts and first indices (build_tiles in moe.hip)
   uint8_t* x8;        // [T, 2H] activation fp8 parts (scaled route)
   uint8_t* xsc;       // [T, scale_pitch(H)] activation e8m0 scales (scaled route)
   void* const* events;  // nullable: 6 hipEvent_t around the 5 stages

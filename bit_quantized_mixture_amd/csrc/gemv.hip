@@ -345,7 +345,8 @@ __global__ void __launch_bounds__(kThreads)
     moe_gemv_kernel(GemvArgs p, const int32_t* __restrict__ tiles,
                     const int32_t* __restrict__ n_tiles, const int32_t* __restrict__ tok,
                     void* __restrict__ out) {
-  const Ptrs pt{tiles, tok, out};
+  // n_tiles: the list's tile count, then the index of its first tile in `tiles`
+  const Ptrs pt{tiles + 4 * n_tiles[1], tok, out};
   constexpr int kLut = FMT == 0 ? kLutBytes : 0;
   constexpr int kOps = ops_per_step<RB>();
   constexpr int kActWait = (kStages - 1) * kOps + 3 * RB;  // loads issued after a step's acts
@@ -447,6 +448,7 @@ __global__ void __launch_bounds__(kThreads)
   const int W = p.ks_waves;
   const int mt = int(blockIdx.x) / p.n_rblocks;
   if (mt >= *n_tiles) return;  // uniform over the workgroup
+  tiles += 4 * n_tiles[1];     // n_tiles: count, then the index of the list's first tile
   const int32_t n_blocks = int32_t(GU ? (p.I + 7) / 8 : (p.N + 15) / 16);
   const int32_t blk = (int(blockIdx.x) % p.n_rblocks) * (kWaves / W) + wave / W;
   const int wi = wave % W;
@@ -1071,19 +1073,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4
   }
 }
 
-int cu_count() {
-  static std::atomic<int> cached[64];  // 0 = not read yet; the value read is idempotent
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cached[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    cached[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
 
 // A list of 16-row tiles: the tile array, its device-side count, a host-side bound, and
 // whether these are the tail tiles of the MFMA-tile path.
@@ -1142,6 +1131,20 @@ hipError_t launch_stage(const GemvArgs& g, const TileList& tl, const MoeLaunch& 
 }
 
 }  // namespace
+
+int cu_count() {
+  static std::atomic<int> cached[64];  // 0 = not read yet; the value read is idempotent
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 // SLOT: activations and h in the slot order of the NF4 MFMA-tile path (tail tiles of that
 // path); otherwise natural order.
@@ -1251,7 +1254,8 @@ hipError_t launch_gemv(const MoeLaunch& L, hipStream_t stream, int stage) {
 }
 
 hipError_t launch_gemv_tails(const MoeLaunch& L, hipStream_t stream, int stage) {
-  const TileList tl{L.tiles + 4 * L.max_mtiles, L.n_mtiles + 1, L.max_stiles, true};
+  // this GEMM's tail tiles: count and first index at n_mtiles[4 + 2 * stage]
+  const TileList tl{L.tiles + 4 * L.max_mtiles, L.n_mtiles + 4 + 2 * stage, L.max_stiles, true};
   return L.fmt == 0 ? launch_gemv_fmt<0, true>(L, tl, stream, stage)
                     : launch_gemv_fmt<1, false>(L, tl, stream, stage);
 }

@@ -519,15 +519,30 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int32_t* wsum, int* t
 }
 
 // One workgroup walks the experts in order and cuts each expert's rows into bm-row tiles.  If
-// the last piece of an expert has at most `tail` rows (tail > 0), it is cut into 16-row
-// tiles instead, listed in tails[] (their count in n_mtiles[1]), so a full-size tile is not
-// spent on a few rows.
+// the last piece of an expert has at most `tail` rows (tail > 0), it becomes a "tail": it is
+// cut into 16-row tiles for the streaming kernel, listed in tails[], so a full-size tile is
+// not spent on a few rows -- unless a long GEMM launch's last round of workgroups has room
+// for it.  The main list holds the regular tiles, then one entry per tail (its rows as a
+// single tile, in expert order; t[3] = index of its first 16-row tile).  For a GEMM whose
+// column sweep has nt tiles, the workgroups of the regular tiles fill
+// R = ceil(regular * nt / n_cu) rounds of the n_cu compute units; when R >= kAbsorbRounds the
+// first j tails, j = (free slots of the last round) / nt, run as main tiles in that round, and
+// only the others go to the streaming kernel.  (In a launch of a few rounds a filled last
+// round costs more than it saves: its workgroups then share the memory system with many
+// more others.)  Counts written to n_mtiles (kTileCounts ints):
+//   [0] regular tiles, [1] 0              (count and first index, the streaming path's list)
+//   [2] gate_up main tiles, [3] down main tiles
+//   [4], [5] gate_up 16-row tail tiles: count, first index in tails[]
+//   [6], [7] the same for down
+constexpr int kAbsorbRounds = 4;
+
 struct TileArgs {
   const int32_t* offsets;
   int E, bm, tail;
   int32_t* tiles;
   int32_t* tails;
   int32_t* n_mtiles;
+  int nt_gu, nt_dn, n_cu;  // column tiles of the two GEMMs, compute units (tails only)
 };
 
 __device__ void build_tiles(const TileArgs& ta) {
@@ -539,6 +554,7 @@ __device__ void build_tiles(const TileArgs& ta) {
   __shared__ int32_t wsum[4];
   const int tid = threadIdx.x;
   int run = 0, run_s = 0;
+  // regular tiles and 16-row tail tiles
   for (int base = 0; base < E; base += 256) {
     const int e = base + tid;
     const int start = e < E ? offsets[e] : 0;
@@ -567,9 +583,46 @@ __device__ void build_tiles(const TileArgs& ta) {
     run += tot;
     run_s += tot_s;
   }
+  // one main entry per tail, after the regular tiles
+  int run_t = 0, run_s2 = 0;
+  for (int base = 0; base < E; base += 256) {
+    const int e = base + tid;
+    const int start = e < E ? offsets[e] : 0;
+    const int cnt = e < E ? offsets[e + 1] - start : 0;
+    const int nfull = cnt / bm, rem = cnt - nfull * bm;
+    const bool split = rem > 0 && rem <= tail;
+    const int ns = split ? (rem + kGemvTileRows - 1) / kGemvTileRows : 0;
+    int tot_t, tot_s;
+    const int ord = run_t + block_exclusive_scan(split ? 1 : 0, wsum, &tot_t);
+    const int first_s = run_s2 + block_exclusive_scan(ns, wsum, &tot_s);
+    if (split) {
+      int32_t* t = tiles + 4 * int64_t(run + ord);
+      t[0] = e;
+      t[1] = start + nfull * bm;
+      t[2] = rem;
+      t[3] = first_s;
+    }
+    run_t += tot_t;
+    run_s2 += tot_s;
+  }
+  __syncthreads();  // the tail entries' first indices are read back below
   if (tid == 0) {
     n_mtiles[0] = run;
-    n_mtiles[1] = run_s;
+    n_mtiles[1] = 0;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int64_t nt = g == 0 ? ta.nt_gu : ta.nt_dn;
+      int j = 0;
+      if (run_t > 0 && nt > 0 && ta.n_cu > 0) {
+        const int64_t wgs = int64_t(run) * nt;
+        const int64_t rounds = (wgs + ta.n_cu - 1) / ta.n_cu;
+        if (rounds >= kAbsorbRounds) j = int(min(int64_t(run_t), (rounds * ta.n_cu - wgs) / nt));
+      }
+      const int s0 = j < run_t ? tiles[4 * int64_t(run + j) + 3] : run_s;
+      n_mtiles[2 + g] = run + j;
+      n_mtiles[4 + 2 * g] = run_s - s0;
+      n_mtiles[5 + 2 * g] = s0;
+    }
   }
 }
 
@@ -577,7 +630,7 @@ __global__ void __launch_bounds__(256) build_tiles_kernel(TileArgs ta) { build_t
 
 hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, int32_t* tiles,
                               int32_t* n_tiles, hipStream_t stream) {
-  const TileArgs ta{offsets, E, bm, 0, tiles, tiles, n_tiles};
+  const TileArgs ta{offsets, E, bm, 0, tiles, tiles, n_tiles, 0, 0, 0};
   hipLaunchKernelGGL(build_tiles_kernel, dim3(1), dim3(256), 0, stream, ta);
   return hipGetLastError();
 }
@@ -663,7 +716,7 @@ static hipError_t launch_stage_tiles(const MoeLaunch& L, GemmArgs g, hipStream_t
   const int64_t n_out = GU ? L.I : L.H;
   const int per_wave = GU ? 32 : 64;
   g.tiles = L.tiles;
-  g.n_mtiles = L.n_mtiles;
+  g.n_mtiles = L.n_mtiles + (GU ? 2 : 3);  // main tiles of this GEMM (regular + absorbed tails)
 
   g.n_ntiles = int((n_out + WAVES * per_wave - 1) / (WAVES * per_wave));
   // XCD-local order when a row tile's column sweep fits one XCD's 32 CUs (one round): its
@@ -716,8 +769,10 @@ static hipError_t launch_fmt(const MoeLaunch& L, hipStream_t stream) {
   const int64_t S = L.T * L.k, nchunks = L.T * L.H / 8;
   const unsigned gx = grid_1d(nchunks > S ? nchunks : S);
   // one launch converts x and builds the tile list (the "build_tiles" stage stays empty)
+  const int wv = L.cfg.waves;
   const TileArgs ta{L.offsets, int(L.E), L.cfg.bm, L.tail_rows, L.tiles,
-                    L.tiles + 4 * L.max_mtiles, L.n_mtiles};
+                    L.tiles + 4 * L.max_mtiles, L.n_mtiles,
+                    int((L.I + 32 * wv - 1) / (32 * wv)), int((L.H + 64 * wv - 1) / (64 * wv)), cu_count()};
   if (FMT == 0 && !L.cfg.gemv)
     hipLaunchKernelGGL(convert_x_kernel<0>, dim3(gx), dim3(256), 0, stream, L.x, L.x16, nchunks,
                        L.slots, S, L.k, L.inv, L.tok, ta);

@@ -315,7 +315,7 @@ hipError_t launch_gate_up_scaled(const MoeLaunch& L, hipStream_t stream) {
   a.wq = L.w_gu;
   a.wsc = reinterpret_cast<const uint8_t*>(L.s_gu);
   a.tiles = L.tiles;
-  a.n_mtiles = L.n_mtiles;
+  a.n_mtiles = L.n_mtiles + 2;  // gate_up main tiles (regular + absorbed tails)
   a.slots = L.slots;
   a.h = L.h;
   a.K = L.H;
