@@ -406,7 +406,22 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
     const int64_t j = int64_t(nt) * (WAVES * 32) + wave * 32 + col;
     _Float16* hout = reinterpret_cast<_Float16*>(p.out);
     const int64_t pos = act_pos<FMT>(j);
-    if (!p.bias && !p.clamped_glu) {
+    if (!p.bias && !p.clamped_glu && rows == BM) {
+      // a full tile: buffer stores with a per-lane offset fixed for the whole epilogue and a
+      // wave-uniform offset per accumulator row, so no per-store address arithmetic runs
+      const uint32_t vo = uint32_t(4 * half * p.I + pos) * 2u;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const __amdgpu_buffer_rsrc_t hres =
+            buffer_rsrc(hout + (int64_t(row0) + 32 * rb) * p.I, uint32_t(32 * p.I * 2));
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t so = uint32_t((8 * (r >> 2) + (r & 3)) * p.I) * 2u;
+          const _Float16 hv = (_Float16)swiglu(acc[rb][0][r], acc[rb][1][r]);
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, hv), hres, int(vo), int(so), 0);
+        }
+      }
+    } else if (!p.bias && !p.clamped_glu) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
@@ -415,7 +430,7 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
           if (row < rows) {
             const float g = acc[rb][0][r];
             const float u = acc[rb][1][r];
-            hout[int64_t(row0 + row) * p.I + pos] = (_Float16)(g / (1.0f + __expf(-g)) * u);
+            hout[int64_t(row0 + row) * p.I + pos] = (_Float16)swiglu(g, u);
           }
         }
       }
@@ -430,7 +445,7 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
           if (row < rows) {
             const float g = acc[rb][0][r] + bg;
             const float u = acc[rb][1][r] + bu;
-            const float hv = p.clamped_glu ? clamped_glu(g, u) : g / (1.0f + __expf(-g)) * u;
+            const float hv = p.clamped_glu ? clamped_glu(g, u) : swiglu(g, u);
             hout[int64_t(row0 + row) * p.I + pos] = (_Float16)hv;
           }
         }

@@ -291,7 +291,7 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_scaled_kernel(ScaledArgs 
       if (row < rows) {
         const float g = acc[rb][0][r] + bg;
         const float u = acc[rb][1][r] + bu;
-        const float hv = p.clamped_glu ? clamped_glu(g, u) : g / (1.0f + __expf(-g)) * u;
+        const float hv = p.clamped_glu ? clamped_glu(g, u) : swiglu(g, u);
         p.h[int64_t(row0 + row) * p.I + j] = (_Float16)hv;
       }
     }

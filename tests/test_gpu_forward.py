@@ -46,6 +46,33 @@ def test_small_layers(e4b, fmt, path, E, H, I, T, k):
     assert_out_is_rne_of_f32(out, out32)
 
 
+@pytest.mark.timeout(300)
+def test_tails_in_the_last_round(e4b):
+    """An expert's short last piece (at most a quarter tile: a tail) runs as one main MFMA tile
+    when its GEMM launch fills at least four rounds of the CUs and the last round has free
+    slots, else as 16-row tiles on the streaming kernel.  This layer (E=16, H=256, I=3200,
+    top-4, T=2048: about 512 rows per expert, 256-row tiles) has several tails; its gate_up
+    launch (25 column tiles per row tile) fills four rounds and takes most of them, its down
+    launch (one column tile, one round) none, so one forward runs absorbed tails, streamed
+    gate_up tails and streamed down tails together."""
+    from oracle import route as oroute
+    E, H, I, T, k = 16, 256, 3200, 2048, 4
+    layer = random_layer(e4b, "nf4", E, H, I, T, k, seed=1)
+    counts = np.bincount(oroute.topk(layer.logits, k).ravel(), minlength=E)
+    bm, tail = 256, 64
+    n_tails = int(sum(1 for c in counts if 0 < c % bm <= tail))
+    regular = int(sum(c // bm if 0 < c % bm <= tail else -(-c // bm) for c in counts))
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    wgs = regular * (-(-I // 128))
+    rounds = -(-wgs // n_cu)
+    absorbed = min(n_tails, (rounds * n_cu - wgs) // (-(-I // 128))) if rounds >= 4 else 0
+    print(f"tails {n_tails}, gate_up: {rounds} rounds, {absorbed} tails as main tiles")
+    assert 0 < absorbed < n_tails, (n_tails, rounds, absorbed)
+    out, out32 = layer.forward(PATHS["auto"])
+    assert_rows_within_tolerance(out32, layer.oracle_out(), "tails in the last round")
+    assert_out_is_rne_of_f32(out, out32)
+
+
 @pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
 @pytest.mark.parametrize("E,H,I,T,k", [
     (4, 2880, 192, 5, 2),      # gate_up K = 2880: 12 K steps, the last partial; few items, so K is
