@@ -10,7 +10,7 @@ Which tokens are checked:
 * "all"   every token of the batch;
 * "tiles" the tokens of the first and last sorted row of every row tile the MFMA-tile path
           cuts (per expert, rows in tiles of bm = 256 when the mean routed rows per expert is
-          at least 256, else 128; a last piece of at most bm / 4 rows cut into 16-row tail
+          at least 512, else 128; a last piece of at most bm / 4 rows cut into 16-row tail
           tiles instead), plus the middle row of every tail tile.  This covers the first and
           last row of every active expert, every tile boundary and every tail tile.
 """
@@ -57,7 +57,7 @@ def _packed(wl, experts):
 def tile_rows(wl, offsets) -> np.ndarray:
     """Sorted rows at the boundaries of the MFMA-tile path's row tiles and tail tiles."""
     S = wl.T * wl.k
-    bm = 256 if S / wl.E >= 256 else 128
+    bm = 256 if S / wl.E >= 512 else 128
     tail = bm // 4
     rows = []
     for e in range(wl.E):
