@@ -9,16 +9,29 @@
 // quantised per token to int8 with s_x = absmax / 127; y[n] = s_x * sum_b s[n, b] * I_b with
 // I_b the exact int32 dot product of block b's codes and the token's int8 codes.
 //
-// GEMV layout: a workgroup of 8 waves owns one tile of <= 16 routed rows of one expert (their
-// tokens' int8 rows staged in LDS) and 128 / ksplit weight rows; the K axis is cut into ksplit
-// parts, one per wave of a row group, summed through LDS at the end in a fixed order.  Lane
-// (r, g) of a wave streams 16 contiguous bytes (one 32-weight block) of row r at block 4c + g
-// of chunk c, so a wave's load covers 64 contiguous bytes of each of 16 rows.  Codes are read
-// as u = q + 8 (the nibble XOR 8, 0..15) so a byte-wise mask gives the dot-product operand;
-// the block sum of the token's codes times 8 is subtracted back (exact):
-//   I_b = sum u * x - 8 * sum x.
-// The activation rows are stored with each group of 8 elements in the order 0,2,4,6,1,3,5,7,
-// the order of the low and high nibbles of a packed dword, so v_dot4 pairs the right elements.
+// GEMV layout (both kernels): a workgroup of 8 waves owns one tile of <= 16 routed rows of one
+// expert (their tokens' int8 rows staged in LDS) and 128 / ksplit weight rows; the K axis is
+// cut into ksplit parts, one per wave of a row group, summed through LDS at the end in a fixed
+// order.
+//
+// int4_gemv_mfma_kernel (tiles of 4 or more routed rows).  Lane (r = lane % 16, g = lane / 16) of a wave streams the 16 bytes (one 32-weight block) of block
+// 4c + g of chunk c of row r, so a wave's load covers 64 contiguous bytes of each of 16 rows.
+// A 4 x 4 transpose across the four 16-lane groups (two permlane32 and two permlane16 swaps)
+// then leaves register j of lane (r, g) with dword g of block 4c + j: the codes of row r at
+// elements 8g .. 8g + 7 of that block, which is how the int8 MFMA 16 x 16 x 32 takes one
+// 32-wide block from 64 lanes.  Each code enters the MFMA as an int8 holding 16 q (the nibble
+// at the top of its byte: one shift and one mask per 4 codes), each token's activations in
+// their stored order, every group of 8 as 0,2,4,6,1,3,5,7 (the low nibbles of a dword, then
+// the high ones), so one MFMA per block gives
+//   D[t][r] = 16 * I_b(row r, token t)   exactly (|D| <= 16 * 8 * 127 * 32 < 2^24),
+// and the block adds D * (s[r, b] / 16) (both factors exact in fp32, one rounding in the FMA,
+// as s * I_b) into lane (r, g)'s fp32 sums of tokens 4g .. 4g + 3.
+//
+// int4_gemv_dot4_kernel (a batch of 1 to 3 tokens, where most of the MFMA's 16 token rows would
+// be padding).  Lane (r = lane / 4, g = lane % 4) streams block 4c + g of row r and takes, for
+// each token of the tile, v_dot4 products of its codes read as u = q + 8 (the nibble XOR 8, a
+// byte-wise mask gives the operand); the block sum of the token's codes times 8 is subtracted
+// back (exact):  I_b = sum u * x - 8 * sum x.  The 4 block lanes of a row are added at the end.
 #include "e4b_device.h"
 #include "e4b_internal.h"
 
@@ -170,7 +183,7 @@ struct I4Args {
   const uint8_t* wq;        // [E, N, K/2]
   const uint16_t* sc;       // [E, N, K/32] fp16 bits
   const int8_t* qx;         // [T, K] int8, permuted groups
-  const int32_t* xs;        // [T, K/32] block sums of qx
+  const int32_t* xs;        // [T, K/32] block sums of qx (dot4 kernel)
   const float* sx;          // [T]
   const int32_t* slots;     // [S] sorted slots
   const int32_t* tiles;     // [max_tiles, 4]: expert, first sorted row, rows, 0
@@ -180,7 +193,129 @@ struct I4Args {
   int32_t k, n_rblocks, tile_rows, ksplit;
 };
 
-__global__ void __launch_bounds__(512) int4_gemv_kernel(I4Args p) {
+// Activation rows in LDS are K + 16 bytes apart, so the 16 token rows of one MFMA operand
+// read (same block, same lane group) fall in 16 different 16-byte bank groups.
+constexpr int kActPad = 16;
+
+__device__ __forceinline__ void swap16(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+__device__ __forceinline__ void swap32(uint32_t& a, uint32_t& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  a = r[0];
+  b = r[1];
+}
+
+__global__ void __launch_bounds__(512) int4_gemv_mfma_kernel(I4Args p) {
+  typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rb = int(blockIdx.x) % p.n_rblocks;
+  const int it = int(blockIdx.x) / p.n_rblocks;
+  if (it >= *p.n_tiles) return;  // uniform
+  const int e = p.tiles[4 * it], row0 = p.tiles[4 * it + 1], ntok = p.tiles[4 * it + 2];
+  const int64_t K = p.K;
+  const int64_t pitch = K + kActPad;
+  const int nb = int(K >> 5);  // blocks per row
+  const int ks = p.ksplit, rows_wg = 16 * (kGvWaves / ks);
+  int8_t* act = reinterpret_cast<int8_t*>(lds);                                  // [tile_rows][pitch]
+  float* part = reinterpret_cast<float*>(lds + int64_t(p.tile_rows) * pitch);   // [rows_wg * ks][16]
+
+  const int kq = wave % ks, rg = wave / ks;
+  const int r = lane & 15, g = lane >> 4;
+  const int rl = 16 * rg + r;                       // row inside the workgroup's block
+  const int64_t n = int64_t(rb) * rows_wg + rl;
+  const int nch = int(K >> 7);                      // 128-weight chunks per row
+  const int c0 = (kq * nch) / ks, c1 = ((kq + 1) * nch) / ks;
+  const uint32_t kb = uint32_t(K >> 1);
+  const __amdgpu_buffer_rsrc_t wres =
+      buffer_rsrc(p.wq + int64_t(e) * p.N * kb, uint32_t(p.N * kb));
+  const __amdgpu_buffer_rsrc_t sres =
+      buffer_rsrc(p.sc + int64_t(e) * p.N * nb, uint32_t(p.N * nb * 2));
+  const uint32_t woff = uint32_t(n) * kb + 16u * g;
+  const uint32_t soff = uint32_t(n) * uint32_t(nb) * 2u;
+  // MFMA A operand: token row r of the tile (rows past the tile's count repeat its last row;
+  // their sums are never stored), the 8 activation bytes of lane group g in a block
+  const int8_t* arow = act + int64_t(r < ntok ? r : ntok - 1) * pitch + 8 * g;
+
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};  // tokens 4g .. 4g + 3 of row r
+
+  // Chunks in groups of 4 with the next group's loads in flight (two register sets); loads
+  // past the wave's last chunk repeat it (in bounds, never used).
+  u32x4 wA[4], wB[4];
+  u32x2 sA[4], sB[4];
+  auto load4 = [&](int cb, u32x4 (&w)[4], u32x2 (&sv)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = cb + j < c1 ? cb + j : c1 - 1;
+      w[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(wres, woff, 64u * c, 0));
+      sv[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(sres, soff, 8u * c, 0));
+    }
+  };
+  auto compute = [&](const u32x4& wv, const u32x2& sv, int c) {
+    uint32_t d[4] = {wv[0], wv[1], wv[2], wv[3]};
+    swap32(d[0], d[2]);
+    swap32(d[1], d[3]);
+    swap16(d[0], d[1]);
+    swap16(d[2], d[3]);
+    i32x4 D[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = (d[j] << 4) & 0xF0F0F0F0u;  // elements 0,2,4,6 of the 8, times 16
+      const uint32_t hi = d[j] & 0xF0F0F0F0u;         // elements 1,3,5,7, times 16
+      const int64_t wop = int64_t((uint64_t(hi) << 32) | lo);
+      const int64_t aop = *reinterpret_cast<const int64_t*>(arow + 32 * (4 * c + j));
+      D[j] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, wop, i32x4{0, 0, 0, 0}, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint16_t sh = uint16_t(j & 1 ? sv[j >> 1] >> 16 : sv[j >> 1] & 0xFFFFu);
+      const float s16 = float(__builtin_bit_cast(_Float16, sh)) * 0.0625f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(s16, float(D[j][i]), acc[i]);
+    }
+  };
+  // the first weight loads go out before the activations are staged, so the two latencies
+  // overlap
+  if (c0 < c1) load4(c0, wA, sA);  // uniform
+  // stage the tile's token rows (int8 codes)
+  const int pieces = int(K >> 4);
+  for (int i = tid; i < ntok * pieces; i += 512) {
+    const int tt = i / pieces, c = i - tt * pieces;
+    const int64_t tok = p.slots[row0 + tt] / p.k;
+    *reinterpret_cast<u32x4*>(act + tt * pitch + 16 * c) =
+        *reinterpret_cast<const u32x4*>(p.qx + tok * K + 16 * c);
+  }
+  __syncthreads();
+  if (c0 < c1) {  // uniform
+    for (int c = c0; c < c1; c += 8) {
+      load4(c + 4, wB, sB);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (c + j < c1) compute(wA[j], sA[j], c + j);
+      load4(c + 8, wA, sA);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (c + 4 + j < c1) compute(wB[j], sB[j], c + 4 + j);
+    }
+  }
+  // the ksplit waves of a row group through LDS, in wave order
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (4 * g + i < ntok) part[(rl * ks + kq) * kGvTok + 4 * g + i] = acc[i];
+  __syncthreads();
+  for (int i = tid; i < rows_wg * ntok; i += 512) {
+    const int tt = i / rows_wg, row = i - tt * rows_wg;
+    float sum = 0.f;
+    for (int q = 0; q < ks; ++q) sum += part[(row * ks + q) * kGvTok + tt];
+    const int64_t tok = p.slots[row0 + tt] / p.k;
+    p.out[int64_t(row0 + tt) * p.N + int64_t(rb) * rows_wg + row] = sum * p.sx[tok];
+  }
+}
+
+__global__ void __launch_bounds__(512) int4_gemv_dot4_kernel(I4Args p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rb = int(blockIdx.x) % p.n_rblocks;
@@ -330,8 +465,17 @@ int int4_gemv_ksplit(int64_t max_tiles, int64_t N, int64_t K) {
   return 8;
 }
 
+// The MFMA kernel for tiles of at least kI4MfmaRows routed rows (a batch of that many tokens),
+// the dot4 kernel below it.  Measured on the 128-expert decode layer's gate_up stack: at 64
+// tokens (tiles of about 4 rows) 67 us against 76 us; at one token the MFMA kernel was no
+// faster on the routed layer and 42 % slower on one dense matrix.
+constexpr int kI4MfmaRows = 4;
+
+bool int4_use_mfma(int64_t T) { return int4_gemv_tile_rows(T) >= kI4MfmaRows; }
+
 size_t int4_gemv_lds_bytes(int64_t T, int64_t K) {
   const int64_t tr = int4_gemv_tile_rows(T);
+  if (int4_use_mfma(T)) return size_t(tr * (K + kActPad) + 128 * kGvTok * 4);
   return size_t(tr * K + tr * (K >> 5) * 4 + 128 * kGvTok * 4);
 }
 
@@ -359,13 +503,17 @@ hipError_t launch_int4_gemv(const Int4GemvLaunch& L, hipStream_t stream) {
   a.n_rblocks = int(L.N / (16 * (kGvWaves / a.ksplit)));
   a.tile_rows = tr;
   const size_t lds = int4_gemv_lds_bytes(L.T, L.K);
+  const void* kern = int4_use_mfma(L.T) ? reinterpret_cast<const void*>(int4_gemv_mfma_kernel)
+                                        : reinterpret_cast<const void*>(int4_gemv_dot4_kernel);
   if (lds > 64 * 1024) {
-    err = hipFuncSetAttribute(reinterpret_cast<const void*>(int4_gemv_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     if (err != hipSuccess) return err;
   }
   const unsigned grid = unsigned(L.max_tiles * a.n_rblocks);
-  hipLaunchKernelGGL(int4_gemv_kernel, dim3(grid), dim3(512), lds, stream, a);
+  if (int4_use_mfma(L.T))
+    hipLaunchKernelGGL(int4_gemv_mfma_kernel, dim3(grid), dim3(512), lds, stream, a);
+  else
+    hipLaunchKernelGGL(int4_gemv_dot4_kernel, dim3(grid), dim3(512), lds, stream, a);
   return hipGetLastError();
 }
 

@@ -64,11 +64,13 @@ def _routed_problem(E, N, K, T, k, seed):
 
 @pytest.mark.parametrize("E,N,K,T,k", [
     (1, 16, 128, 1, 1),        # dense M = 1, one chunk per row
+    (2, 32, 256, 2, 1),        # two tokens: the dot4 kernel's largest tile
+    (5, 64, 512, 4, 2),        # four tokens: the MFMA kernel's smallest tile
     (3, 48, 256, 5, 2),        # ragged experts
     (4, 160, 640, 40, 2),      # experts with more than 16 routed rows: several token tiles
     (8, 256, 1024, 64, 8),     # every expert busy
     (2, 128, 8192, 3, 1),      # the largest K
-    (4, 64, 8192, 20, 2),      # 16-row tiles at the largest K: 155 KB of LDS per workgroup
+    (4, 64, 8192, 20, 2),      # 16-row tiles at the largest K: 136 KB of LDS per workgroup
 ])
 def test_int4_gemv_matches_oracle(e4b, E, N, K, T, k):
     w, x, logits = _routed_problem(E, N, K, T, k, seed=E * 100 + T)

@@ -24,7 +24,7 @@ ALLOWED = [
     (r"moe_decode_step_kernel", 16),
 ]
 HOT = [r"moe_gemm_kernel", r"moe_gemm_scaled_kernel", r"moe_gemv_kernel", r"moe_gemv_ks_kernel",
-       r"dgrad_kernel", r"int4_gemv_kernel", r"moe_decode_step_kernel", r"combine_kernel",
+       r"dgrad_kernel", r"int4_gemv_mfma_kernel", r"int4_gemv_dot4_kernel", r"moe_decode_step_kernel", r"combine_kernel",
        r"pack_nf4_kernel", r"pack_mxfp4_kernel", r"topk_kernel", r"scatter_kernel"]
 
 
