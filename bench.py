@@ -309,7 +309,7 @@ def blas_threads() -> str:
 
 
 def batch_report(torch, layer: Layer, T: int, steps: int, warmup: int, flush: int = 0, flags: int = 0,
-                 graph: bool = False, variant: dict | None = None):
+                 graph: bool = False, variant: dict | None = None, counters: bool = True):
     b = Batch(layer, T, flags)
     b.variant = variant or {}
     wl = b.wl
@@ -317,7 +317,7 @@ def batch_report(torch, layer: Layer, T: int, steps: int, warmup: int, flush: in
     m = measure(torch, b, steps, warmup, flush)
     # the counters were taken at each workload's own T; other batch sizes get none
     key = wl.name if wl.T == WORKLOADS[wl.name].T else f"{wl.name}_T{wl.T}"
-    rl = roofline(wl, n_active, m, None if flush else load_counters(key))
+    rl = roofline(wl, n_active, m, None if (flush or not counters) else load_counters(key))
     S = wl.T * wl.k
     ms = m["ms_per_step"]
     rep = {
@@ -547,6 +547,13 @@ def main():
     secondary = {}
     sections = set() if args.no_secondary else (
         {"dgrad", "prefill", "int4", "decode"} if args.secondary == "all" else set(args.secondary.split(",")))
+    if "prefill" in sections and not args.flags & e4b.E4B_COMBINE_ATOMIC:
+        # the same layer with the atomic scatter-combine in the down GEMM (E4B_COMBINE_ATOMIC);
+        # the counters in profiles/ were taken on the ordered combine, so no traffic figure
+        key = wl.name + "_atomic_combine"
+        secondary[key] = batch_report(torch, layer, wl.T, args.steps, args.warmup,
+                                      flags=args.flags | e4b.E4B_COMBINE_ATOMIC, counters=False)
+        log(fmt_rep(key, secondary[key]) + f"; stages {secondary[key]['stage_ms']}")
     del layer
     torch.cuda.empty_cache()
     ceiling = hbm_ceiling(torch, e4b)

@@ -14,7 +14,7 @@ import torch
 
 __all__ = [
     "E4BError", "E4B_FMT_NF4", "E4B_FMT_MXFP4", "E4B_PATH_AUTO", "E4B_PATH_GEMM", "E4B_PATH_GEMV",
-    "E4B_ROUTE_RENORMALIZE", "E4B_ACT_CLAMPED_GLU", "E4B_GU_INTERLEAVED", "E4B_MXFP4_SCALED", "E4B_MXFP4_FP16", "lib_path", "e4b_version", "e4b_status_string", "e4b_pack_nf4",
+    "E4B_ROUTE_RENORMALIZE", "E4B_ACT_CLAMPED_GLU", "E4B_GU_INTERLEAVED", "E4B_MXFP4_SCALED", "E4B_MXFP4_FP16", "E4B_COMBINE_ATOMIC", "lib_path", "e4b_version", "e4b_status_string", "e4b_pack_nf4",
     "e4b_pack_mxfp4", "e4b_route_workspace_bytes", "e4b_route_permute", "e4b_moe_workspace_bytes",
     "e4b_moe_forward", "e4b_moe_forward_noalloc", "e4b_noalloc_scratch_bytes", "e4b_stream_probe", "e4b_decode_workspace_bytes", "e4b_moe_decode_step", "MoeArgs", "e4b_dgrad_workspace_bytes", "e4b_grouped_dgrad", "DgradArgs",
 ]
@@ -25,6 +25,7 @@ E4B_TILE_AUTO, E4B_TILE_32, E4B_TILE_128, E4B_TILE_256 = 0x0, 0x4, 0x8, 0xC
 E4B_ROUTE_RENORMALIZE = 1
 E4B_ACT_CLAMPED_GLU, E4B_GU_INTERLEAVED = 0x10, 0x20
 E4B_MXFP4_SCALED, E4B_MXFP4_FP16 = 0x40, 0x80
+E4B_COMBINE_ATOMIC = 0x100
 _FMT = {"nf4": E4B_FMT_NF4, "mxfp4": E4B_FMT_MXFP4, E4B_FMT_NF4: E4B_FMT_NF4, E4B_FMT_MXFP4: E4B_FMT_MXFP4}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

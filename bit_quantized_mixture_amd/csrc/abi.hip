@@ -160,7 +160,7 @@ int check_forward_shape(const e4b_moe_args* a) {
   if (a->E <= 0 || a->H <= 0 || a->I <= 0 || a->T < 0 || a->k < 1) return E4B_ERR_ARG;
   if (a->k > a->E) return E4B_ERR_ARG;
   if ((a->flags & ~(E4B_PATH_MASK | E4B_TILE_MASK | E4B_ACT_CLAMPED_GLU | E4B_GU_INTERLEAVED |
-                    E4B_MXFP4_ROUTE_MASK)) != 0 ||
+                    E4B_MXFP4_ROUTE_MASK | E4B_COMBINE_ATOMIC)) != 0 ||
       (a->flags & E4B_MXFP4_ROUTE_MASK) == E4B_MXFP4_ROUTE_MASK ||
       (a->flags & E4B_PATH_MASK) == 3)
     return E4B_ERR_ARG;
@@ -454,6 +454,7 @@ int forward_impl(const e4b_moe_args* a, char* ws, hipStream_t stream) {
   M.b_dn = a->b_dn;
   M.clamped_glu = (a->flags & E4B_ACT_CLAMPED_GLU) ? 1 : 0;
   M.interleaved = (a->flags & E4B_GU_INTERLEAVED) ? 1 : 0;
+  M.atomic_combine = ((a->flags & E4B_COMBINE_ATOMIC) && !L.gemv) ? 1 : 0;
   M.x16 = reinterpret_cast<_Float16*>(ws + L.off_x16);
   M.h = reinterpret_cast<_Float16*>(ws + L.off_h);
   M.y = reinterpret_cast<float*>(ws + L.off_y);

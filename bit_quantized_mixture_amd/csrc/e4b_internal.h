@@ -57,10 +57,13 @@ struct MoeLaunch {
   int clamped_glu;    // activation: 0 silu(G) * U, 1 clamped GLU
   int interleaved;    // gate_up rows: 0 halves, 1 interleaved
   int scaled;         // MXFP4 gate_up on the block-scaled fp8 x fp4 instruction (MFMA tiles)
+  int atomic_combine; // MFMA tile path: the down GEMM adds topk_w * y into a [T, H] float32
+                      // accumulator (out_f32, else the y region) with atomic adds
   // workspace carve-outs
   _Float16* x16;   // [T, H]
   _Float16* h;     // [S, I]
-  float* y;        // [S, H], sorted-row order
+  float* y;        // [S, H], sorted-row order (atomic combine: the [T, H] accumulator when
+                   // out_f32 is NULL)
   int32_t* inv;    // [S]: slot -> sorted row
   int32_t* tok;    // [S]: sorted row -> token (slot / k)
   int32_t* tiles;  // [max_mtiles + max_stiles, 4]: main tiles, then tail tiles

@@ -76,6 +76,11 @@ struct GemvArgs {
   int32_t interleaved;     // gate_up rows: 0 halves (gate j, up I + j), 1 interleaved
   const float* bias;       // nullable [E, N], added to the products
   int32_t ks_waves;        // K-split kernel: waves per 16-row block (1, 2, 4 or 8)
+  // down, MFMA path's tail tiles only: nullable [T, N] float32 accumulator; when set,
+  // topk_w[slots[p]] * y of sorted row p is added to row tok[p] atomically instead of stored
+  float* comb;
+  const int32_t* slots;
+  const float* topk_w;
 };
 
 // Index arrays read with uniform addresses inside the persistent loop are separate
@@ -330,12 +335,20 @@ __device__ __forceinline__ void store_block(const GemvArgs& p, const Ptrs& pt,
       }
     }
   } else if (r < st.rows) {
-    float* y = reinterpret_cast<float*>(pt.out) + int64_t(st.row0 + r) * p.N;
     const int32_t n0 = blk * 16 + 4 * g;
     if (n0 < int32_t(p.N)) {  // N % 64 == 0
       f32x4 v = acc;
       if (p.bias) v += *reinterpret_cast<const f32x4*>(p.bias + int64_t(st.e) * p.N + n0);
-      *reinterpret_cast<f32x4*>(y + n0) = v;
+      if (p.comb) {
+        const float w = p.topk_w[p.slots[st.row0 + r]];
+        float* dst = p.comb + int64_t(pt.tok[st.row0 + r]) * p.N + n0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          (void)__hip_atomic_fetch_add(dst + i, w * v[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        float* y = reinterpret_cast<float*>(pt.out) + int64_t(st.row0 + r) * p.N;
+        *reinterpret_cast<f32x4*>(y + n0) = v;
+      }
     }
   }
 }
@@ -1171,6 +1184,11 @@ static hipError_t launch_gemv_fmt(const MoeLaunch& L, const TileList& tl, hipStr
   g.sc = L.s_dn;
   g.K = L.I;
   g.N = L.H;
+  if (L.atomic_combine && tl.tails) {  // the MFMA path's accumulator (see launch_fmt)
+    g.comb = L.out_f32 ? L.out_f32 : L.y;
+    g.slots = L.slots;
+    g.topk_w = L.topk_w;
+  }
   return launch_stage<FMT, false, SLOT>(g, tl, L, L.y, L.H, stream);
 }
 

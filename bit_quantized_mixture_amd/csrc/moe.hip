@@ -15,6 +15,8 @@
 //   gemm<DN>      y[p, n] = h[p] . Wd[e,n]   (sorted row p)
 //   combine       out[t] = sum_j topk_w[s] * y[inv[s]], s = t*k+j  (fixed order) -> fp32, bf16
 //                 (RNE); inv (slot -> sorted row) is written by convert_x
+//   (atomic combine: gemm<DN> adds topk_w[s] * y straight into a [T, H] fp32 accumulator that
+//   convert_x cleared, and the last pass only rounds it to bf16)
 //
 // Tile structure of gemm: a workgroup owns BM rows of one expert and WAVES*64 weight rows
 // (GU: 32 gate + 32 matching up rows per wave, so SwiGLU is formed in registers).  Each
@@ -58,6 +60,9 @@ struct GemmArgs {
   int32_t clamped_glu;     // GU activation: 0 silu(G) * U, 1 clamped GLU
   int32_t interleaved;     // GU rows: 0 halves (gate j, up I + j), 1 interleaved (2j, 2j + 1)
   int32_t xcd_order;       // 1: workgroup ids dealt to the 8 XCDs in contiguous chunks
+  const float* topk_w;     // DN with comb: routing weight of each slot [T * k_top]
+  float* comb;             // DN: nullable [T, N] float32; when set, topk_w[slot] * y is added
+                           // there atomically instead of y being stored
 };
 
 
@@ -451,6 +456,48 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
         }
       }
     }
+  } else if (p.comb) {
+    // weighted scatter-combine: row p of the tile belongs to slot s = slots[row0 + p], token
+    // s / k; its products go to comb[token] scaled by topk_w[s].  The token offsets and
+    // weights of the tile's rows are staged in LDS (the activation ring is free once every
+    // wave has left the main loop), then read back with one address per lane half.
+    int32_t* s_toff = reinterpret_cast<int32_t*>(smem);
+    float* s_w = reinterpret_cast<float*>(smem + BM * 4);
+    __syncthreads();
+    for (int i = tid; i < BM; i += WAVES * 64) {
+      int32_t toff = 0;
+      float w = 0.0f;
+      if (i < rows) {
+        const int32_t sl = p.slots[row0 + i];
+        toff = (sl / p.k_top) * int32_t(p.N);  // T * N < 2^31
+        w = p.topk_w[sl];
+      }
+      s_toff[i] = toff;
+      s_w[i] = w;
+    }
+    __syncthreads();
+    float bn[2] = {0.0f, 0.0f};
+    if (p.bias) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f) bn[f] = p.bias[int64_t(e) * p.N + nrow[f]];
+    }
+    const bool full = rows == BM && int64_t(nt + 1) * (WAVES * 64) <= p.N;  // uniform
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = 32 * rb + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (full || row < rows) {
+          float* dst = p.comb + s_toff[row];
+          const float w = s_w[row];
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+            if (full || nvalid[f])
+              (void)__hip_atomic_fetch_add(dst + nrow[f], w * (acc[rb][f][r] + bn[f]),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
   } else {
     float* y = reinterpret_cast<float*>(p.out);
     const bool full = rows == BM && int64_t(nt + 1) * (WAVES * 64) <= p.N;  // uniform
@@ -653,7 +700,9 @@ hipError_t launch_build_tiles(const int32_t* offsets, int E, int bm, int32_t* ti
 // x bf16 -> fp16 (exact for |x| in fp16's normal range), stored in the k-slot order of the
 // weight format inside each aligned group of 8.  Also inverts the routing permutation,
 // inv[slots[p]] = p for the S sorted rows p, and records each sorted row's token,
-// tok[p] = slots[p] / k.  The last workgroup first builds the tile list (build_tiles).
+// tok[p] = slots[p] / k.  The last workgroup first builds the tile list (build_tiles).  With
+// `zero` set it also clears that [T, H] float32 accumulator of the atomic combine (kernel
+// stores, not a memset, so the sequence can be captured in a graph).
 template <int FMT>
 __global__ void __launch_bounds__(256) convert_x_kernel(const uint16_t* __restrict__ x,
                                                         _Float16* __restrict__ x16,
@@ -662,6 +711,7 @@ __global__ void __launch_bounds__(256) convert_x_kernel(const uint16_t* __restri
                                                         int64_t S, int32_t k,
                                                         int32_t* __restrict__ inv,
                                                         int32_t* __restrict__ tok,
+                                                        float* __restrict__ zero,
                                                         TileArgs ta) {
   if (blockIdx.x == gridDim.x - 1) build_tiles(ta);  // uniform over the workgroup
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
@@ -684,6 +734,10 @@ __global__ void __launch_bounds__(256) convert_x_kernel(const uint16_t* __restri
 #pragma unroll
     for (int i = 0; i < 8; ++i) o[FMT == 0 ? nf4_elem_slot(i) : i] = v[i];
     *reinterpret_cast<f16x8*>(x16 + 8 * q) = o;
+    if (zero) {
+      reinterpret_cast<f32x4*>(zero + 8 * q)[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      reinterpret_cast<f32x4*>(zero + 8 * q)[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   }
 }
 
@@ -712,6 +766,19 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   }
 }
 
+// out[t, :] = bf16 RNE of the atomic combine's accumulator acc [T, H] (n4 = T * H / 4).
+__global__ void __launch_bounds__(256) round_out_kernel(const float* __restrict__ acc, int64_t n4,
+                                                        uint16_t* __restrict__ out) {
+  const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t q = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; q < n4; q += stride) {
+    const f32x4 s = reinterpret_cast<const f32x4*>(acc)[q];
+    u32x2 o;
+    o[0] = uint32_t(f32_to_bf16_rne(s[0])) | (uint32_t(f32_to_bf16_rne(s[1])) << 16);
+    o[1] = uint32_t(f32_to_bf16_rne(s[2])) | (uint32_t(f32_to_bf16_rne(s[3])) << 16);
+    reinterpret_cast<u32x2*>(out)[q] = o;
+  }
+}
+
 static unsigned grid_1d(int64_t work, int per_block = 256) {
   int64_t g = (work + per_block - 1) / per_block;
   if (g < 1) g = 1;
@@ -726,6 +793,9 @@ static void record(const MoeLaunch& L, int i, hipStream_t stream) {
 // One grouped GEMM stage over the main tiles, then the streaming kernel over the 16-row tail
 // tiles if any (an expert's last few rows: streaming its weights once per 16 rows beats
 // running them as a mostly empty MFMA tile).
+// The [T, H] float32 accumulator of the atomic combine.
+static float* combine_target(const MoeLaunch& L) { return L.out_f32 ? L.out_f32 : L.y; }
+
 template <int FMT, bool GU, int BM, int WAVES>
 static hipError_t launch_stage_tiles(const MoeLaunch& L, GemmArgs g, hipStream_t stream) {
   const int64_t n_out = GU ? L.I : L.H;
@@ -774,6 +844,8 @@ static hipError_t launch_gemms(const MoeLaunch& L, hipStream_t stream) {
   g.out = L.y;
   g.K = L.I;
   g.N = L.H;
+  g.topk_w = L.topk_w;
+  g.comb = L.atomic_combine ? combine_target(L) : nullptr;
   return launch_stage_tiles<FMT, false, BM, WAVES>(L, g, stream);
 }
 
@@ -788,12 +860,13 @@ static hipError_t launch_fmt(const MoeLaunch& L, hipStream_t stream) {
   const TileArgs ta{L.offsets, int(L.E), L.cfg.bm, L.tail_rows, L.tiles,
                     L.tiles + 4 * L.max_mtiles, L.n_mtiles,
                     int((L.I + 32 * wv - 1) / (32 * wv)), int((L.H + 64 * wv - 1) / (64 * wv)), cu_count()};
+  float* zero = L.atomic_combine ? combine_target(L) : nullptr;
   if (FMT == 0 && !L.cfg.gemv)
     hipLaunchKernelGGL(convert_x_kernel<0>, dim3(gx), dim3(256), 0, stream, L.x, L.x16, nchunks,
-                       L.slots, S, L.k, L.inv, L.tok, ta);
+                       L.slots, S, L.k, L.inv, L.tok, zero, ta);
   else
     hipLaunchKernelGGL(convert_x_kernel<1>, dim3(gx), dim3(256), 0, stream, L.x, L.x16, nchunks,
-                       L.slots, S, L.k, L.inv, L.tok, ta);
+                       L.slots, S, L.k, L.inv, L.tok, zero, ta);
   record(L, 1, stream);
   record(L, 2, stream);
   hipError_t err;
@@ -809,8 +882,12 @@ static hipError_t launch_fmt(const MoeLaunch& L, hipStream_t stream) {
     err = launch_gemms<FMT, 32, 1>(L, stream);
   if (err != hipSuccess) return err;
   record(L, 4, stream);
-  hipLaunchKernelGGL(combine_kernel, dim3(grid_1d(L.T * L.H / 4)), dim3(256), 0, stream, L.y,
-                     L.topk_w, L.inv, L.T, L.H, L.k, L.out, L.out_f32);
+  if (L.atomic_combine)
+    hipLaunchKernelGGL(round_out_kernel, dim3(grid_1d(L.T * L.H / 4)), dim3(256), 0, stream,
+                       combine_target(L), L.T * L.H / 4, L.out);
+  else
+    hipLaunchKernelGGL(combine_kernel, dim3(grid_1d(L.T * L.H / 4)), dim3(256), 0, stream, L.y,
+                       L.topk_w, L.inv, L.T, L.H, L.k, L.out, L.out_f32);
   record(L, 5, stream);
   return hipGetLastError();
 }

@@ -118,6 +118,19 @@ typedef enum e4b_fmt { E4B_FMT_NF4 = 0, E4B_FMT_MXFP4 = 1 } e4b_fmt;
 #define E4B_MXFP4_SCALED 0x40
 #define E4B_MXFP4_FP16 0x80
 #define E4B_MXFP4_ROUTE_MASK 0xC0
+/* e4b_moe_args.flags bit 8: how the down GEMM's results reach the token rows (the weighted
+ * combine among the grouped-nf4-gemm 0.25.0 glue kernels, project description opening
+ * section).  Clear (the default, deterministic): the down GEMM writes one float32 row per
+ * routed slot ([T*k, H] in the workspace) and a last pass sums each token's k rows in slot
+ * order, so repeated calls give identical bits.  E4B_COMBINE_ATOMIC, on the MFMA tile path:
+ * the down GEMM adds topk_w * (its product) straight into a float32 [T, H] accumulator
+ * (out_f32 when given, else the workspace) with device-scope float32 atomic adds, and the
+ * last pass only rounds it to bf16; no per-slot rows are written.  The order of a token's k
+ * additions then depends on scheduling, so the last bits of out and out_f32 may differ from
+ * call to call (each result stays within the same error bound).  On the streaming path
+ * (E4B_PATH_GEMV, or AUTO choosing it) the flag is accepted and the combine stays the
+ * deterministic one. */
+#define E4B_COMBINE_ATOMIC 0x100
 
 /*
  * e4b_pack_nf4 — quantise bf16 expert stacks to NF4.
@@ -187,7 +200,8 @@ typedef struct e4b_moe_args {
   float* out_f32;         /* [T, H] float32 out, or NULL: the value `out` is rounded from */
   void* ws;               /* device workspace of at least e4b_moe_workspace_bytes() */
   size_t ws_bytes;
-  int32_t flags;          /* E4B_PATH_* | E4B_TILE_* */
+  int32_t flags;          /* E4B_PATH_* | E4B_TILE_* | E4B_ACT_* | E4B_GU_* | E4B_MXFP4_* |
+                           * E4B_COMBINE_ATOMIC */
   int32_t reserved;       /* must be 0 */
   /* NULL, or 6 hipEvent_t the call records on `stream` around its 5 stages (x conversion,
    * tile map, gate_up GEMM, down GEMM, combine), so a caller can time each kernel on the

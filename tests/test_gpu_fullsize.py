@@ -10,6 +10,9 @@ computed while the test runs (tests/fullsize_oracle.py, which calls only oracle/
   tile and of every 16-row tail tile (so every active expert's first and last row, every tile
   boundary and every tail tile).
 
+The MFMA-path layers run a second time with the atomic weighted scatter-combine
+(E4B_COMBINE_ATOMIC), checked against the same oracle values.
+
 Checked per case: the routing of the whole batch bit-exact (ids, offsets, slots) and its
 weights to float32 precision; on the checked tokens, the fp32 output within the per-row bound
 of the float64 oracle, the bf16 output the round-to-nearest-even of the fp32 output (on every
@@ -30,21 +33,38 @@ from moe_inputs import WORKLOADS, make_bias, make_expert_weight, make_logits, ma
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-# (case, workload, T override, checked tokens, expert variant); grouped by workload so the
-# packed stacks (GPU and oracle) are reused by consecutive cases
+ATOMIC = 0x100  # E4B_COMBINE_ATOMIC
+# (case, workload, T override, checked tokens, expert variant, flags); grouped by workload so
+# the packed stacks (GPU and oracle) and the oracle values are reused by consecutive cases
 CASES = [
-    ("tiny_nf4", "tiny_nf4", None, "all", False),
-    ("mixtral_nf4_prefill", "mixtral_nf4_prefill", None, "tiles", False),
-    ("finegrained_nf4_decode_T1", "finegrained_nf4_decode", 1, "all", False),
-    ("finegrained_nf4_decode_T4", "finegrained_nf4_decode", 4, "all", False),
-    ("finegrained_nf4_decode_T16", "finegrained_nf4_decode", 16, "all", False),
-    ("finegrained_nf4_decode_T64", "finegrained_nf4_decode", 64, "all", False),
-    ("mxfp4_moe", "mxfp4_moe", None, "all", False),
-    ("mxfp4_moe_clamped_glu", "mxfp4_moe", None, "all", True),
-    ("skewed_nf4_prefill", "skewed_nf4_prefill", None, "tiles", False),
+    ("tiny_nf4", "tiny_nf4", None, "all", False, 0),
+    ("mixtral_nf4_prefill", "mixtral_nf4_prefill", None, "tiles", False, 0),
+    ("mixtral_nf4_prefill_atomic_combine", "mixtral_nf4_prefill", None, "tiles", False, ATOMIC),
+    ("finegrained_nf4_decode_T1", "finegrained_nf4_decode", 1, "all", False, 0),
+    ("finegrained_nf4_decode_T4", "finegrained_nf4_decode", 4, "all", False, 0),
+    ("finegrained_nf4_decode_T16", "finegrained_nf4_decode", 16, "all", False, 0),
+    ("finegrained_nf4_decode_T64", "finegrained_nf4_decode", 64, "all", False, 0),
+    ("mxfp4_moe", "mxfp4_moe", None, "all", False, 0),
+    ("mxfp4_moe_atomic_combine", "mxfp4_moe", None, "all", False, ATOMIC),
+    ("mxfp4_moe_clamped_glu", "mxfp4_moe", None, "all", True, 0),
+    ("mxfp4_moe_clamped_glu_atomic_combine", "mxfp4_moe", None, "all", True, ATOMIC),
+    ("skewed_nf4_prefill", "skewed_nf4_prefill", None, "tiles", False, 0),
+    ("skewed_nf4_prefill_atomic_combine", "skewed_nf4_prefill", None, "tiles", False, ATOMIC),
 ]
 
 _packed_cache = {}
+_ref_cache = {}
+
+
+def oracle_values(wl, mode, variant, r_off, r_slots, r_ids, r_w):
+    """Checked tokens, oracle and comparator outputs of a case; kept for the next case of the
+    same workload, batch and variant (the combine mode does not change them)."""
+    key = (wl.name, wl.T, mode, variant)
+    if key not in _ref_cache:
+        _ref_cache.clear()
+        toks = fo.checked_tokens(wl, mode, r_off, r_slots)
+        _ref_cache[key] = (toks,) + tuple(fo.expected(wl, toks, r_ids, r_w, variant))
+    return _ref_cache[key]
 
 
 def packed_layer(e4b, wl):
@@ -66,8 +86,8 @@ def packed_layer(e4b, wl):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("case,name,T,mode,variant", CASES, ids=[c[0] for c in CASES])
-def test_full_size(e4b, case, name, T, mode, variant, record_property):
+@pytest.mark.parametrize("case,name,T,mode,variant,flags", CASES, ids=[c[0] for c in CASES])
+def test_full_size(e4b, case, name, T, mode, variant, flags, record_property):
     wl = WORKLOADS[name] if T is None else WORKLOADS[name].with_T(T)
     print(f"\n{case}: GPU forward", flush=True)
     packed = packed_layer(e4b, wl)
@@ -81,7 +101,8 @@ def test_full_size(e4b, case, name, T, mode, variant, record_property):
         kw = dict(act="clamped_glu", interleaved=True,
                   b_gu=torch.from_numpy(make_bias(wl, "gate_up")).to(DEV),
                   b_dn=torch.from_numpy(make_bias(wl, "down")).to(DEV))
-    out, out32 = e4b.e4b_moe_forward(wl.fmt, x, gp, gs, dp, ds, w, off, slots, wl.k, out_f32=True, **kw)
+    out, out32 = e4b.e4b_moe_forward(wl.fmt, x, gp, gs, dp, ds, w, off, slots, wl.k, out_f32=True,
+                                     path=flags, **kw)
     torch.cuda.synchronize()
     o32, ob = host(out32), host(out)
     assert np.all(np.isfinite(o32))
@@ -94,9 +115,8 @@ def test_full_size(e4b, case, name, T, mode, variant, record_property):
     np.testing.assert_array_equal(host(slots), r_slots)
     np.testing.assert_allclose(host(w), r_w, rtol=2e-6, atol=1e-7)
 
-    toks = fo.checked_tokens(wl, mode, r_off, r_slots)
+    toks, ref, cmp_ = oracle_values(wl, mode, variant, r_off, r_slots, r_ids, r_w)
     print(f"{case}: oracle on {len(toks)} of {wl.T} tokens", flush=True)
-    ref, cmp_ = fo.expected(wl, toks, r_ids, r_w, variant)
     worst = assert_rows_within_tolerance(o32[toks], ref, case)
 
     # fidelity (P11): fused error below dequantise-to-bf16 error
