@@ -105,7 +105,7 @@ def test_forward_rejects_bad_arguments(e4b):
     assert f(E=0) == ERR_ARG
     assert f(T=-1) == ERR_ARG
     assert f(flags=3) == ERR_ARG
-    assert f(flags=0x100) == ERR_ARG                 # unknown bit
+    assert f(flags=0x200) == ERR_ARG                 # unknown bit
     assert f(flags=0xC0) == ERR_ARG                  # both MXFP4 routes
     assert f(flags=0x40) not in (ERR_ARG, ERR_SHAPE)   # one MXFP4 route is accepted
     assert f(flags=0x30) not in (ERR_ARG, ERR_SHAPE)   # expert-variant bits are accepted
