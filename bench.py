@@ -586,6 +586,12 @@ def main():
                 secondary[key] = batch_report(torch, lay, wv.T, max(args.steps, 10), args.warmup,
                                               variant=variant)
                 log(fmt_rep(key, secondary[key]))
+                # the gate_up on the block-scaled fp8 x fp4 instruction (E4B_MXFP4_SCALED); the
+                # counters in profiles/ were taken on the default route, so no traffic figure
+                key = name + "_scaled_route"
+                secondary[key] = batch_report(torch, lay, wv.T, max(args.steps, 10), args.warmup,
+                                              flags=e4b.E4B_MXFP4_SCALED, counters=False)
+                log(fmt_rep(key, secondary[key]))
         del lay
         torch.cuda.empty_cache()
     if "int4" in sections:
