@@ -179,6 +179,9 @@ def test_workspace_sizes_cover_the_intermediates(e4b):
         S = wl.T * wl.k
         assert n >= 2 * wl.T * wl.H + 2 * S * wl.I + 4 * S * wl.H
         assert n < 2 * (2 * wl.T * wl.H + 2 * S * wl.I + 4 * S * wl.H) + (1 << 20)
+        # the atomic combine keeps its [T, H] float32 accumulator in the same layout
+        na = e4b.e4b_moe_workspace_bytes(wl.fmt, wl.E, wl.H, wl.I, wl.T, wl.k, e4b.E4B_COMBINE_ATOMIC)
+        assert na == n and na >= 4 * wl.T * wl.H
 
 
 def test_dgrad_rejects_bad_arguments(e4b):
