@@ -454,13 +454,19 @@ hipError_t launch_quant_act(const uint16_t* x, int64_t T, int64_t K, int8_t* q, 
 int int4_gemv_tile_rows(int64_t T) { return int(T < kGvTok ? T : kGvTok); }
 
 int int4_gemv_ksplit(int64_t max_tiles, int64_t N, int64_t K) {
-  // The smallest K split (with whole row blocks) that gives the chip >= 8192 waves, short of
-  // a split that would leave a wave fewer than 4 chunks of 128 weights.
+  // The smallest K split (with whole row blocks) that gives the chip at least 6 waves per CU
+  // (the tile count is the host's upper bound), short of a split that would leave a wave fewer
+  // than 4 chunks of 128 weights.  Measured per call against the earlier target of 8192 waves
+  // (alternating runs on one box): one dense [14336, 4096] matrix at M = 1 16.3 against 20.0
+  // us (split 2 instead of 8), the 128-expert gate_up stack at 4 tokens 24.5 against 38.9 us
+  // (1 instead of 4); 1 and 64 tokens within noise.  Larger splits leave each wave one round
+  // of loads and spend the time in the workgroup's cross-wave sum.
+  const int64_t want = 6 * int64_t(cu_count());
   for (int ks = 1; ks <= 8; ks <<= 1) {
     const int64_t rows_wg = 16 * (kGvWaves / ks);
     if (N % rows_wg) continue;
     const int64_t waves = max_tiles * (N / rows_wg) * kGvWaves;
-    if (waves >= 8192 || ks == 8 || (K >> 7) < 4 * 2 * ks) return ks;
+    if (waves >= want || ks == 8 || (K >> 7) < 4 * 2 * ks) return ks;
   }
   return 8;
 }

@@ -65,6 +65,8 @@ def _routed_problem(E, N, K, T, k, seed):
 @pytest.mark.parametrize("E,N,K,T,k", [
     (1, 16, 128, 1, 1),        # dense M = 1, one chunk per row
     (2, 32, 256, 2, 1),        # two tokens: the dot4 kernel's largest tile
+    (2, 128, 256, 2, 1),       # dot4 kernel, K not split (one wave per 16 rows takes all of K)
+    (3, 256, 1024, 3, 2),      # dot4 kernel, K split over 2 waves
     (5, 64, 512, 4, 2),        # four tokens: the MFMA kernel's smallest tile
     (3, 48, 256, 5, 2),        # ragged experts
     (4, 160, 640, 40, 2),      # experts with more than 16 routed rows: several token tiles
