@@ -87,6 +87,35 @@ def test_int4_gemv_matches_oracle(e4b, E, N, K, T, k):
     _assert_gemv_close(got, ref, mag, K, f"E={E} N={N} K={K} T={T} k={k}")
 
 
+@pytest.mark.parametrize("E", [4096, 4100])
+def test_int4_gemv_many_experts_hand_routed(e4b, E):
+    """1-3 tokens run as one launch (tile lookup and activation quantisation inside the GEMV)
+    up to 4096 experts, and as quantiser + GEMV launches above: both against the oracle, on a
+    routing written by hand (the router takes at most 1024 experts), with an all-zero token."""
+    N, K, T, k = 16, 128, 3, 2
+    rng = np.random.default_rng(E)
+    w = f32_to_bf16_bits((0.02 * rng.standard_normal((E, N, K))).astype(np.float32))
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    x[1] = 0.0
+    xb = f32_to_bf16_bits(x)
+    ids = np.array([[5, E - 1], [5, 17], [E - 96, E - 1]])   # token t, choice j -> expert
+    order = sorted(range(T * k), key=lambda s_: (ids.flat[s_], s_ // k))
+    slots = np.array(order, np.int32)
+    counts = np.bincount(ids.ravel(), minlength=E)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    packed, scales = e4b.e4b_pack_int4_b32(dev_bf16(w))
+    out = e4b.e4b_gemv_int4_b32(packed, scales, dev_bf16(xb), k, torch.from_numpy(off).to(DEV),
+                                torch.from_numpy(slots).to(DEV))
+    torch.cuda.synchronize()
+    used = sorted(set(ids.ravel().tolist()))
+    op, os_ = oi4.quantize_pack(w[used])
+    off_u = np.concatenate([[0], np.cumsum(counts[used])]).astype(np.int32)
+    ref, mag = oi4.grouped_gemv(op, os_, xb, k, off_u, slots)
+    got = host(out)
+    assert np.all(np.isfinite(got))
+    _assert_gemv_close(got, ref, mag, K, f"E={E}")
+
+
 def test_int4_gemv_is_deterministic(e4b):
     w, x, logits = _routed_problem(4, 128, 1024, 24, 2, 9)
     packed, scales = e4b.e4b_pack_int4_b32(dev_bf16(w))
