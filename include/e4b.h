@@ -384,7 +384,9 @@ int e4b_int4_gemv_workspace_bytes(const e4b_int4_gemv_args* a, size_t* bytes);
  * over routed MoE experts).  For every sorted row p of expert e (token t = sorted_slots[p] / k):
  *   out_f32[p, n] = s_x[t] * sum_b s[e, n, b] * I_b,
  * I_b = sum over the 32 k of block b of q[e, n, k] * q_x[t, k], an exact int32 sum, with q_x,
- * s_x the activations of e4b_quantize_act_int8 (recomputed inside, in the workspace).  The
+ * s_x the activations of e4b_quantize_act_int8, recomputed inside the call: into the workspace
+ * by a quantiser launch, or, for 1-3 tokens and at most 4096 experts, by each workgroup of the
+ * GEMV for its own token rows (the same arithmetic, so the same codes; one launch).  The
  * block terms are summed in float32 in a fixed order: deterministic.  A dense layer is the
  * case E = 1, k = 1.  Synchronous errors as e4b_moe_forward.
  */
