@@ -113,3 +113,21 @@ def test_atomic_combine_repeated_calls_and_graph(e4b):
         assert_out_is_rne_of_f32(host(out), host(out32))
         step()  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_atomic_combine_random_shapes(e4b, case):
+    """Seeded random shapes (as in the random-shape forward tests) with the atomic combine on the
+    MFMA tile path, every row-tile size."""
+    rng = np.random.default_rng(5000 + case)
+    fmt = ("nf4", "mxfp4")[case % 2]
+    E = int(rng.integers(1, 25))
+    k = int(rng.integers(1, min(E, 8) + 1))
+    H, I = 64 * int(rng.integers(1, 17)), 64 * int(rng.integers(1, 13))
+    T = int(rng.integers(1, 600))
+    flags = 0x1 | (0x0, 0x4, 0x8, 0xC)[case % 4]
+    layer = random_layer(e4b, fmt, E, H, I, T, k, seed=6000 + case)
+    out, out32 = layer.forward(flags | ATOMIC)
+    what = f"case {case}: {fmt} E={E} H={H} I={I} T={T} k={k} flags={flags:#x}"
+    assert_rows_within_tolerance(out32, layer.oracle_out(), what)
+    assert_out_is_rne_of_f32(out, out32)

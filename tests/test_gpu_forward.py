@@ -46,6 +46,29 @@ def test_small_layers(e4b, fmt, path, E, H, I, T, k):
     assert_out_is_rne_of_f32(out, out32)
 
 
+@pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
+@pytest.mark.parametrize("T", [1100, 1050])
+def test_all_tokens_on_one_expert(e4b, fmt, T):
+    """A router biased so that every token picks expert 3 (top-1): one expert holds every row
+    (a mean of 69 rows per expert, so 128-row tiles: 8 full tiles and a 76-row last tile at
+    T = 1100, 8 and a 26-row tail on the streaming kernel at T = 1050), the other 15 none."""
+    bias = np.zeros(16, np.float32)
+    bias[3] = 40.0
+    layer = random_layer(e4b, fmt, 16, 256, 192, T, 1, seed=T, logit_bias=bias)
+    out, out32 = layer.forward(PATHS["auto"])
+    assert_rows_within_tolerance(out32, layer.oracle_out(), f"{fmt} one expert T={T}")
+    assert_out_is_rne_of_f32(out, out32)
+
+
+@pytest.mark.parametrize("fmt", ["nf4", "mxfp4"])
+def test_every_expert_for_every_token(e4b, fmt):
+    """k = E = 64, the largest top-k the router takes: each token's row goes to all 64 experts."""
+    layer = random_layer(e4b, fmt, 64, 128, 64, 20, 64, seed=64)
+    out, out32 = layer.forward(PATHS["auto"])
+    assert_rows_within_tolerance(out32, layer.oracle_out(), f"{fmt} k=E=64")
+    assert_out_is_rne_of_f32(out, out32)
+
+
 @pytest.mark.timeout(300)
 def test_tails_in_the_last_round(e4b):
     """An expert's short last piece (at most a quarter tile: a tail) runs as one main MFMA tile
