@@ -71,22 +71,6 @@ __device__ __forceinline__ uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel)
 //     and the 64 lookups of a wave never conflict.  64 KB.
 constexpr int kNf4LutBytes = 256 * 64 * 4;
 
-// fp16 bit patterns of the codebook (form (1) above, as 16-bit values), code 0..15.
-__device__ __constant__ const uint16_t kNf4Half[16] = {
-    0xBC00, 0xB992, 0xB833, 0xB652, 0xB48D, 0xB1EA, 0xADD4, 0x0000,
-    0x2D18, 0x3126, 0x33E0, 0x3568, 0x370D, 0x3880, 0x39C9, 0x3C00};
-
-// Fill the table at `lut` (kNf4LutBytes of LDS) with `nthreads` threads of the workgroup
-// (nthreads divides 256 * 16); visible to other waves after the next barrier.
-__device__ __forceinline__ void nf4_lut_fill(uint8_t* lut, int tid, int nthreads) {
-  typedef uint32_t v4 __attribute__((ext_vector_type(4)));
-  for (int c = tid; c < 256 * 16; c += nthreads) {  // 16-byte chunks: value c / 16
-    const int v = c >> 4;
-    const uint32_t pair = uint32_t(kNf4Half[v >> 4]) | (uint32_t(kNf4Half[v & 15]) << 16);
-    *reinterpret_cast<v4*>(lut + 16 * c) = v4{pair, pair, pair, pair};
-  }
-}
-
 // Decode one packed NF4 dword (8 codes) through the LDS table to 8 fp16 codebook values in
 // element order: out[b] = (element 2b, element 2b+1).  lanebase = lane * 4.  One v_perm
 // builds each lookup address (byte value << 8 | lanebase).
@@ -121,6 +105,21 @@ __device__ __forceinline__ void nf4_decode8(uint32_t w, uint32_t out[4]) {
   out[1] = perm(hi_even, lo_even, 0x07030602u);  // elements 4, 6
   out[2] = perm(hi_odd, lo_odd, 0x05010400u);    // elements 1, 3
   out[3] = perm(hi_odd, lo_odd, 0x07030602u);    // elements 5, 7
+}
+
+// Fill the table of (3) at `lut` (kNf4LutBytes of LDS) with `nthreads` threads of the
+// workgroup (nthreads divides 256 * 16); visible to other waves after the next barrier.  The
+// pair of byte value v comes from the register decode of a dword whose byte 0 is v (element 0
+// = high nibble in the low half of out[0], element 1 = low nibble in the low half of out[2]),
+// so the fill makes no memory access and can run while a kernel's first loads are in flight.
+__device__ __forceinline__ void nf4_lut_fill(uint8_t* lut, int tid, int nthreads) {
+  typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+  for (int c = tid; c < 256 * 16; c += nthreads) {  // 16-byte chunks: value c / 16
+    uint32_t d[4];
+    nf4_decode8(uint32_t(c >> 4), d);
+    const uint32_t pair = (d[0] & 0xFFFFu) | (d[2] << 16);
+    *reinterpret_cast<v4*>(lut + 16 * c) = v4{pair, pair, pair, pair};
+  }
 }
 
 // NF4 block scales enter the fp16 decode multiplied by 2^8, and every fp32 product sum over

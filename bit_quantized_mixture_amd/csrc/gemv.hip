@@ -378,7 +378,6 @@ __global__ void __launch_bounds__(kThreads)
   const int nsteps = my_items * nseg;
   const int last = nsteps - 1;
 
-  if (FMT == 0) nf4_lut_fill(lut, tid, kThreads);
 
   // Ring of kStages register sets: step s uses set s % kStages and LDS buffer s % 2; the loads
   // of steps s + 1 .. s + kStages - 1 (and step s's own weights, until first used) are in
@@ -404,6 +403,10 @@ __global__ void __launch_bounds__(kThreads)
     issue_step<FMT, GU, RB>(p, pt, ci[b], wave, lane, R[b]);
     advance(cur, cst);
   }
+  // the table is filled while the first loads are in flight (the fill makes no memory
+  // access, so the loop's memory-counter waits are unchanged); the first step's barrier
+  // publishes it to every wave
+  if (FMT == 0) nf4_lut_fill(lut, tid, kThreads);
   constexpr int kPeriod = kStages % 2 ? 2 * kStages : kStages;  // (register set, LDS buffer)
   for (int s = 0; s < nsteps; s += kPeriod) {
 #pragma unroll
