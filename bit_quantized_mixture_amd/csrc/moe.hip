@@ -794,12 +794,12 @@ static void record(const MoeLaunch& L, int i, hipStream_t stream) {
   if (L.events) (void)hipEventRecord(reinterpret_cast<hipEvent_t>(L.events[i]), stream);
 }
 
-// One grouped GEMM stage over the main tiles, then the streaming kernel over the 16-row tail
-// tiles if any (an expert's last few rows: streaming its weights once per 16 rows beats
-// running them as a mostly empty MFMA tile).
 // The [T, H] float32 accumulator of the atomic combine.
 static float* combine_target(const MoeLaunch& L) { return L.out_f32 ? L.out_f32 : L.y; }
 
+// One grouped GEMM stage over the main tiles, then the streaming kernel over the 16-row tail
+// tiles if any (an expert's last few rows: streaming its weights once per 16 rows beats
+// running them as a mostly empty MFMA tile).
 template <int FMT, bool GU, int BM, int WAVES>
 static hipError_t launch_stage_tiles(const MoeLaunch& L, GemmArgs g, hipStream_t stream) {
   const int64_t n_out = GU ? L.I : L.H;
