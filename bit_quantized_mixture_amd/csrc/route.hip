@@ -60,10 +60,23 @@ __global__ void __launch_bounds__(256) count_kernel(const int32_t* __restrict__ 
 // One workgroup: offsets[e] = exclusive prefix sum over experts of the total counts,
 // offsets[E] = T*k; then cc[c][e] becomes the first slot of (chunk c, expert e):
 // offsets[e] + sum of cc[c'][e] over c' < c.
+// Up to kCcLds counts are first copied into LDS by the whole workgroup (all loads in flight at
+// once), so the per-expert sums over chunks read LDS instead of waiting on one global load after
+// another (skewed 64-expert layer, 16 chunks: the whole routing call 56.3 -> 53.1 us).
+constexpr int kCcLds = 8192;
+
 __global__ void __launch_bounds__(256) offsets_kernel(int32_t* __restrict__ cc, int chunks, int E,
                                                       int32_t* __restrict__ offsets) {
   __shared__ int32_t wsum[4];
+  __shared__ int32_t s_cc[kCcLds];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t n = int64_t(chunks) * E;
+  const bool staged = n <= kCcLds;  // uniform
+  if (staged) {
+    for (int i = tid; i < int(n); i += 256) s_cc[i] = cc[i];
+    __syncthreads();
+  }
+  auto count = [&](int c, int e) { return staged ? s_cc[c * E + e] : cc[int64_t(c) * E + e]; };
   constexpr int kPer = 4;  // experts per thread (E <= 1024)
   int tot[kPer];
   int mine = 0;
@@ -72,7 +85,7 @@ __global__ void __launch_bounds__(256) offsets_kernel(int32_t* __restrict__ cc, 
     const int e = tid * kPer + i;
     int t = 0;
     if (e < E)
-      for (int c = 0; c < chunks; ++c) t += cc[int64_t(c) * E + e];
+      for (int c = 0; c < chunks; ++c) t += count(c, e);
     tot[i] = t;
     mine += t;
   }
@@ -93,7 +106,7 @@ __global__ void __launch_bounds__(256) offsets_kernel(int32_t* __restrict__ cc, 
       offsets[e] = run;
       int base = run;
       for (int c = 0; c < chunks; ++c) {
-        const int v = cc[int64_t(c) * E + e];
+        const int v = count(c, e);
         cc[int64_t(c) * E + e] = base;
         base += v;
       }
