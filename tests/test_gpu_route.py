@@ -44,7 +44,10 @@ def test_route_skewed_has_empty_experts(e4b):
                                    (8, 1024, 64), (8, 200, 5), (2, 65, 3), (6, 300, 64), (9, 128, 8),
                                    (300, 1024, 64), (70, 65, 3), (257, 16, 2),
                                    # several 1024-token chunks of the counting sort, ragged last
-                                   (2500, 1024, 8), (3073, 3, 2), (1024, 7, 7), (1025, 1, 1)])
+                                   (2500, 1024, 8), (3073, 3, 2), (1024, 7, 7), (1025, 1, 1),
+                                   # chunk counts staged in LDS (9 x 910 = 8190 of at most 8192)
+                                   # and read from memory (9 x 1024)
+                                   (9000, 910, 2), (9000, 1024, 2)])
 def test_route_edge_shapes(e4b, T, E, k):
     rng = np.random.default_rng(T * 1000 + E + k)
     _check(e4b, rng.standard_normal((T, E), dtype=np.float32), k)
