@@ -308,6 +308,14 @@ def blas_threads() -> str:
         return "BLAS threads unknown"
 
 
+def expert_variant(torch, wl) -> dict:
+    """e4b_moe_forward keywords of the MXFP4 family's expert variant: gate/up rows read as
+    interleaved, clamped GLU, the seeded biases of moe_inputs.make_bias."""
+    return dict(act="clamped_glu", interleaved=True,
+                b_gu=torch.from_numpy(make_bias(wl, "gate_up")).to("cuda:0"),
+                b_dn=torch.from_numpy(make_bias(wl, "down")).to("cuda:0"))
+
+
 def batch_report(torch, layer: Layer, T: int, steps: int, warmup: int, flush: int = 0, flags: int = 0,
                  graph: bool = False, variant: dict | None = None, counters: bool = True):
     b = Batch(layer, T, flags)
@@ -315,8 +323,11 @@ def batch_report(torch, layer: Layer, T: int, steps: int, warmup: int, flush: in
     wl = b.wl
     n_active = b.active_experts()
     m = measure(torch, b, steps, warmup, flush)
-    # the counters were taken at each workload's own T; other batch sizes get none
+    # the counters were taken at each workload's own T; other batch sizes get none; the expert
+    # variant has rows of its own
     key = wl.name if wl.T == WORKLOADS[wl.name].T else f"{wl.name}_T{wl.T}"
+    if b.variant:
+        key += "_clamped_glu"
     rl = roofline(wl, n_active, m, None if (flush or not counters) else load_counters(key))
     S = wl.T * wl.k
     ms = m["ms_per_step"]
@@ -524,6 +535,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flags", type=lambda v: int(v, 0), default=0,
                     help="e4b_moe_args.flags for the headline workload (path / tile override)")
+    ap.add_argument("--variant", action="store_true",
+                    help="run the headline workload as the MXFP4 family's expert variant (clamped "
+                         "GLU, interleaved gate/up rows, the seeded biases)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the layer runs on a "
@@ -542,7 +556,8 @@ def main():
     log(f"[bench] device {torch.cuda.get_device_name(0)}; workload {wl.name}, T = {wl.T}")
     layer = Layer(e4b, torch, wl)
     pack_gbs = layer.pack_bytes / layer.pack_s / 1e9
-    main_rep = batch_report(torch, layer, wl.T, args.steps, args.warmup, flags=args.flags)
+    main_rep = batch_report(torch, layer, wl.T, args.steps, args.warmup, flags=args.flags,
+                            variant=expert_variant(torch, wl) if args.variant else None)
     log(fmt_rep(wl.name, main_rep) + f"; stages {main_rep['stage_ms']}")
     secondary = {}
     sections = set() if args.no_secondary else (
@@ -576,12 +591,9 @@ def main():
             secondary[name] = batch_report(torch, lay, WORKLOADS[name].T, max(args.steps, 10), args.warmup)
             log(fmt_rep(name, secondary[name]))
             if name == "mxfp4_moe":
-                # the same layer as the MXFP4 family's expert variant: gate/up rows read as
-                # interleaved, clamped GLU, the seeded biases of moe_inputs.make_bias
+                # the same layer as the MXFP4 family's expert variant
                 wv = WORKLOADS[name]
-                variant = dict(act="clamped_glu", interleaved=True,
-                               b_gu=torch.from_numpy(make_bias(wv, "gate_up")).to("cuda:0"),
-                               b_dn=torch.from_numpy(make_bias(wv, "down")).to("cuda:0"))
+                variant = expert_variant(torch, wv)
                 key = name + "_clamped_glu"
                 secondary[key] = batch_report(torch, lay, wv.T, max(args.steps, 10), args.warmup,
                                               variant=variant)
@@ -637,7 +649,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic (seeded N(0,1) x and logits, N(0,0.02) bf16 weights packed on the GPU)",
-        "config": {"workload": wl.name, "fmt": wl.fmt, "E": wl.E, "H": wl.H, "I": wl.I, "k": wl.k,
+        "config": {"workload": wl.name + ("_clamped_glu" if args.variant else ""), "fmt": wl.fmt,
+                   "E": wl.E, "H": wl.H, "I": wl.I, "k": wl.k,
                    "T": wl.T, "global_batch": wl.T, "parallelism": "single GPU"},
         "tflops": main_rep["tflops"],
         "stage_ms": main_rep["stage_ms"],
