@@ -411,20 +411,33 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
     const int64_t j = int64_t(nt) * (WAVES * 32) + wave * 32 + col;
     _Float16* hout = reinterpret_cast<_Float16*>(p.out);
     const int64_t pos = act_pos<FMT>(j);
-    if (!p.bias && !p.clamped_glu && rows == BM) {
+    if (rows == BM) {
       // a full tile: buffer stores with a per-lane offset fixed for the whole epilogue and a
-      // wave-uniform offset per accumulator row, so no per-store address arithmetic runs
+      // wave-uniform offset per accumulator row, so no per-store address arithmetic runs.
+      // One copy of the store loop per activation form keeps the selection out of the loop.
       const uint32_t vo = uint32_t(4 * half * p.I + pos) * 2u;
+      auto store_full = [&](auto act) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        const __amdgpu_buffer_rsrc_t hres =
-            buffer_rsrc(hout + (int64_t(row0) + 32 * rb) * p.I, uint32_t(32 * p.I * 2));
+        for (int rb = 0; rb < RB; ++rb) {
+          const __amdgpu_buffer_rsrc_t hres =
+              buffer_rsrc(hout + (int64_t(row0) + 32 * rb) * p.I, uint32_t(32 * p.I * 2));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t so = uint32_t((8 * (r >> 2) + (r & 3)) * p.I) * 2u;
-          const _Float16 hv = (_Float16)swiglu(acc[rb][0][r], acc[rb][1][r]);
-          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, hv), hres, int(vo), int(so), 0);
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t so = uint32_t((8 * (r >> 2) + (r & 3)) * p.I) * 2u;
+            const _Float16 hv = (_Float16)act(acc[rb][0][r], acc[rb][1][r]);
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, hv), hres, int(vo), int(so), 0);
+          }
         }
+      };
+      if (!p.bias && !p.clamped_glu) {
+        store_full([](float g, float u) { return swiglu(g, u); });
+      } else {
+        const float bg = p.bias ? p.bias[int64_t(e) * p.N + nrow[0]] : 0.0f;
+        const float bu = p.bias ? p.bias[int64_t(e) * p.N + nrow[1]] : 0.0f;
+        if (p.clamped_glu)
+          store_full([=](float g, float u) { return clamped_glu(g + bg, u + bu); });
+        else
+          store_full([=](float g, float u) { return swiglu(g + bg, u + bu); });
       }
     } else if (!p.bias && !p.clamped_glu) {
 #pragma unroll
