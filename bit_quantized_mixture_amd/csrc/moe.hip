@@ -411,10 +411,12 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
     const int64_t j = int64_t(nt) * (WAVES * 32) + wave * 32 + col;
     _Float16* hout = reinterpret_cast<_Float16*>(p.out);
     const int64_t pos = act_pos<FMT>(j);
-    if (rows == BM) {
+    if (rows == BM && (RB <= 4 || (!p.bias && !p.clamped_glu))) {
       // a full tile: buffer stores with a per-lane offset fixed for the whole epilogue and a
       // wave-uniform offset per accumulator row, so no per-store address arithmetic runs.
-      // One copy of the store loop per activation form keeps the selection out of the loop.
+      // One copy of the store loop per activation form keeps the selection out of the loop;
+      // 256-row tiles keep the guarded loop below for the bias and clamped-GLU forms, since
+      // further copies there take the kernel past its 256 VGPRs.
       const uint32_t vo = uint32_t(4 * half * p.I + pos) * 2u;
       auto store_full = [&](auto act) {
 #pragma unroll
@@ -431,7 +433,7 @@ __global__ void __launch_bounds__(WAVES * 64) moe_gemm_kernel(GemmArgs p) {
       };
       if (!p.bias && !p.clamped_glu) {
         store_full([](float g, float u) { return swiglu(g, u); });
-      } else {
+      } else if constexpr (RB <= 4) {
         const float bg = p.bias ? p.bias[int64_t(e) * p.N + nrow[0]] : 0.0f;
         const float bu = p.bias ? p.bias[int64_t(e) * p.N + nrow[1]] : 0.0f;
         if (p.clamped_glu)
