@@ -205,6 +205,8 @@ VARIANT_CASES = [
     ("nf4", 0xC, 2, 256, 256, 270, 2),      # 256-row tiles + streaming tail tiles (slot order)
     ("mxfp4", 0xC, 2, 256, 320, 270, 2),    # the same in MXFP4 (natural order tails)
     ("nf4", 0x4, 4, 256, 256, 64, 2),       # 32-row tiles
+    ("nf4", 0x8, 2, 256, 256, 300, 2),      # 128-row tiles: full tiles (buffer-store epilogue) + a partial one
+    ("mxfp4", 0x8, 2, 256, 320, 300, 2),    # the same in MXFP4
     ("mxfp4", 0x2, 16, 256, 256, 16, 4),    # streaming path
     ("nf4", 0x0, 16, 512, 256, 8, 4),       # automatic: streaming path
 ]
@@ -224,9 +226,10 @@ def test_clamped_glu_interleaved_with_biases(e4b, fmt, flags, E, H, I, T, k):
         assert_out_is_rne_of_f32(out, out32)
 
 
-@pytest.mark.parametrize("flags", [0x0, 0x2])
+@pytest.mark.parametrize("flags", [0x0, 0x2, 0x8])
 def test_swiglu_with_one_bias_and_interleaved_rows(e4b, flags):
-    E, H, I, T, k = 8, 256, 256, 48 if flags == 0x2 else 400, 2
+    # 0x8: two experts of ~400 rows on 128-row tiles, so most tiles are full
+    E, H, I, T, k = 2 if flags == 0x8 else 8, 256, 256, 48 if flags == 0x2 else 400, 2
     layer = random_layer(e4b, "nf4", E, H, I, T, k, seed=31 + flags)
     rng = np.random.default_rng(5)
     b_gu = rng.standard_normal((E, 2 * I)).astype(np.float32)
