@@ -1,7 +1,9 @@
 """Host logic of bench.py (no GPU): the roofline entry, the storage cost per weight, the
 kernel-source hash that keys the committed HBM counters, and the one-GPU guard."""
+import glob
 import hashlib
 import os
+import re
 import subprocess
 import sys
 
@@ -77,3 +79,17 @@ def test_more_than_one_gpu_is_refused_with_a_message():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_profile_summaries_name_the_present_kernel_sources():
+    """Every committed trace/counter summary of the forward kernels states the hash of the
+    sources it was taken on; it must be the present one."""
+    sha = bench.kernel_source_sha()
+    seen = 0
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.txt"))):
+        with open(path) as f:
+            text = f.read()
+        for m in re.finditer(r"kernel sources sha ([0-9a-f]{16})", text):
+            assert m.group(1) == sha, os.path.basename(path)
+            seen += 1
+    assert seen >= 6
